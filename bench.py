@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention step on one MI355X.
+
+One step = the whole hot path on synthetic inputs already resident in HBM:
+
+* the decode step of a Qwen3-8B-shaped layer (32 q / 8 kv heads, head_dim 128,
+  bf16, batch 256, lognormal context lengths, page_size 1 by default) as one
+  replay of the captured HIP graph: store_kv of the 256 new tokens, then
+  split-K decode attention (and its merge);
+* a ragged causal prefill/extend step (Qwen3-0.6B heads, 8 requests, extend
+  U[128, 2048] on a cached prefix U[0, 1024]): store_kv, then MFMA prefill
+  attention.
+
+``value`` is the decode leg's achieved HBM bandwidth (algorithmic bytes / leg
+time); the same line carries req-tokens/s of the decode leg and the prefill
+leg's TFLOP/s, a roofline object for the dominant kernel (decode attention,
+timed with HIP events on its own stream) and the fp64 CPU oracle timed on the
+same decode workload as a reported baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic HBM bytes of one decode-attention launch: every visible
+    token's K and V slice once per kv head, q in, out written, one 4-byte
+    page-table id per visible token."""
+    e = w.dtype.itemsize
+    L = int(w.seq_lens.long().sum())
+    kv = L * w.kv_heads * w.head_dim * 2 * e
+    qo = 2 * w.bs * w.q_heads * w.head_dim * e
+    return kv + qo + 4 * L
+
+
+def store_bytes(w) -> int:
+    e = w.dtype.itemsize
+    return 2 * 2 * w.num_tokens * w.kv_heads * w.head_dim * e + 4 * w.num_tokens
+
+
+def prefill_flops(w) -> float:
+    """Matrix flops of the unmasked (query, key) pairs: 2 matmuls x 2 flop x d per pair and head."""
+    ext = (w.seq_lens - w.cached_lens).double()
+    C = w.cached_lens.double()
+    pairs = float((ext * C + ext * (ext + 1) / 2).sum())
+    return 4.0 * w.head_dim * w.q_heads * pairs
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--page-size", type=int, default=1, choices=(1, 16))
+    ap.add_argument("--chunk", type=int, default=0, help="decode split size (0 = library default)")
+    ap.add_argument("--kernel-iters", type=int, default=20, help="eager decode launches timed for the roofline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-reqs", type=int, default=256,
+                    help="decode requests the CPU oracle is timed on (first N of the batch)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this attention step has no cross-GPU path "
+              "(the design for sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    from paged_kv_attention_slots_amd import _lib, runner, workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    log("building decode workload (Qwen3-8B shape, bs 256) on the GPU")
+    w4 = wl.qwen3_8b_decode(page_size=args.page_size, device=dev)
+    log(f"  sum(L)={int(w4.seq_lens.sum())} max L={int(w4.seq_lens.max())} ({time.time() - t0:.1f}s)")
+    w3 = wl.ragged_prefill(device=dev)
+    log(f"  prefill tokens={w3.num_tokens} ctx={int(w3.seq_lens.sum())} ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream(device=dev)
+    # fixed buffers recorded by the graph
+    out4 = torch.empty_like(w4.q)
+    lse4 = torch.empty(w4.bs, w4.q_heads, dtype=torch.float32, device=dev)
+    ws4 = _lib.decode_workspace(w4.bs, w4.q_heads, w4.head_dim, w4.max_seq_len, args.chunk, device=dev)
+    k_pool4, v_pool4 = w4.k_pool, w4.v_pool
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph = _lib.msgl_decode_graph_create(k_pool4, v_pool4, w4.k_new, w4.v_new, w4.out_loc, out4, lse4,
+                                              w4.q, w4.page_table, w4.table_idx, w4.seq_lens,
+                                              w4.max_seq_len, ws4, page_size=w4.page_size,
+                                              chunk=args.chunk, sm_scale=w4.sm_scale, stream=stream)
+    out3 = torch.empty_like(w3.q)
+    lse3 = torch.empty(w3.num_tokens, w3.q_heads, dtype=torch.float32, device=dev)
+    max_ext3 = int((w3.seq_lens - w3.cached_lens).max())
+
+    def prefill_leg():
+        _lib.msgl_store_kv(w3.k_pool, w3.v_pool, w3.k_new, w3.v_new, w3.out_loc, stream=stream)
+        _lib.msgl_prefill_attn(out3, lse3, w3.q, w3.k_pool, w3.v_pool, w3.page_table, w3.table_idx,
+                               w3.seq_lens, w3.cached_lens, w3.cu_q, max_ext3, page_size=w3.page_size,
+                               sm_scale=w3.sm_scale, stream=stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        graph.launch(stream)
+        prefill_leg()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        a, b, c = ev[i]
+        a.record(stream)
+        graph.launch(stream)
+        b.record(stream)
+        prefill_leg()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    dec_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    pre_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    ms_per_step = wall * 1e3 / K
+
+    # dominant kernel: decode attention on its own, eager, HIP events on its stream
+    log(f"timing {args.kernel_iters} eager decode-attention launches")
+    ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        runner.decode_attn(w4, k_pool4, v_pool4, out=out4, lse=lse4, workspace=ws4, chunk=args.chunk,
+                           stream=stream)
+    torch.cuda.synchronize()
+    ka.record(stream)
+    for _ in range(args.kernel_iters):
+        runner.decode_attn(w4, k_pool4, v_pool4, out=out4, lse=lse4, workspace=ws4, chunk=args.chunk,
+                           stream=stream)
+    kb.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = ka.elapsed_time(kb) / args.kernel_iters
+
+    dbytes = decode_bytes(w4)
+    sbytes = store_bytes(w4)
+    flops3 = prefill_flops(w3)
+    value = (dbytes + sbytes) / (dec_ms * 1e-3) / 1e9
+    attn_gbs = dbytes / (attn_ms * 1e-3) / 1e9
+    prefill_tflops = flops3 / (pre_ms * 1e-3) / 1e12
+    req_tok_s = w4.bs / (dec_ms * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        n = max(1, min(args.cpu_sample_reqs, w4.bs))
+        log(f"CPU oracle on the first {n} decode requests (host copies)")
+        ws = wl.subset_decode(w4, n)
+        kp_h, vp_h = oracle.store_kv(w4.k_pool.cpu(), w4.v_pool.cpu(), ws.k_new, ws.v_new, ws.out_loc)
+        q_h = ws.q.cpu()
+        args_h = (ws.page_table.cpu(), ws.table_idx.cpu(), ws.seq_lens.cpu(), ws.cu_q.cpu())
+        threads = oracle.num_threads()
+        c0 = time.perf_counter()
+        oracle.attention(q_h, kp_h, vp_h, *args_h)
+        cpu_s = time.perf_counter() - c0
+        sb = decode_bytes(ws)
+        cpu = {"value": round(sb / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"fp64 C oracle, decode attention of the first {n} of {w4.bs} requests "
+                         f"({int(ws.seq_lens.sum())} context tokens), {cpu_s:.2f} s on "
+                         f"{threads} OpenMP threads ({platform.processor() or platform.machine()})",
+               "seconds": round(cpu_s, 3)}
+        log(f"  oracle {cpu_s:.2f}s with {threads} threads")
+
+    rec = {
+        "metric": "paged decode-attn achieved HBM GB/s + req-tokens/s; prefill attn TFLOP/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"qwen3-8b decode bs256 ps{w4.page_size} (hipGraph: store_kv + decode attn) "
+                        f"+ ragged prefill 8 req (store_kv + prefill attn)",
+            "decode": {"batch": w4.bs, "q_heads": w4.q_heads, "kv_heads": w4.kv_heads,
+                       "head_dim": w4.head_dim, "page_size": w4.page_size,
+                       "context_tokens": int(w4.seq_lens.sum()), "max_len": int(w4.seq_lens.max()),
+                       "chunk": args.chunk or 256},
+            "prefill": {"requests": w3.bs, "q_heads": w3.q_heads, "kv_heads": w3.kv_heads,
+                        "head_dim": w3.head_dim, "extend_tokens": w3.num_tokens,
+                        "context_tokens": int(w3.seq_lens.sum())},
+        },
+        "decode_leg_ms": round(dec_ms, 4),
+        "prefill_leg_ms": round(pre_ms, 4),
+        "req_tokens_per_s": round(req_tok_s, 1),
+        "prefill_tflops": round(prefill_tflops, 2),
+        "prefill_frac_of_bf16_peak": round(prefill_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode attention (split + merge), eager, bs 256",
+                     "bytes_per_launch": dbytes, "avg_launch_ms": round(attn_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    graph.destroy()
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

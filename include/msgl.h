@@ -1,0 +1,195 @@
+/*
+ * msgl.h - C ABI of the paged-KV attention step for AMD Instinct MI355X (gfx950).
+ *
+ * One transformer layer's attention step as the Mini-SGLang engine runs it:
+ * the new tokens' K/V are written into a paged KV pool at out_loc, then every
+ * request attends (causal, grouped-query) over its history, gathered through
+ * its page-table row.  Sources: "mini-sglang from Scratch, Engine and sampler"
+ * (sections on initialisation order and the hand-driven engine), "Stage 4
+ * milestone" (section 'What it prints' and the table 'What each chapter
+ * adds'), and the Mini-SGLang Engine article's per-layer pipeline (the KV
+ * write precedes attention).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers named *_pool, q, out, lse, k_new, v_new, page_table, table_idx,
+ * seq_lens, cached_lens, cu_q, out_loc and workspace are DEVICE pointers owned
+ * by the caller; the library never frees or retains them (except a captured
+ * graph, which records them; see msgl_decode_graph_create).  `stream` is a
+ * hipStream_t passed as void* (NULL = the null stream).  Calls only enqueue
+ * work: they never allocate device memory, never synchronise with the host
+ * and never copy between host and device, so they may be recorded into a HIP
+ * graph.  Device faults therefore surface at the caller's next synchronisation.
+ *
+ * Layouts:
+ *   k_pool, v_pool  [num_slots, kv_heads, head_dim], contiguous; the engine's
+ *                   per-layer pool (num_pages + 1, page_size, kv_heads,
+ *                   head_dim) flattened, slot = page * page_size + offset;
+ *                   the last page belongs to the dummy request.
+ *   page_table      int32 [rows, row_stride] row-major; entry [r, j] is the
+ *                   slot of token j of the request in row r (token-level slot
+ *                   ids at every page size).
+ *   q, out          [tokens, q_heads, head_dim]; k_new, v_new [tokens,
+ *                   kv_heads, head_dim]; all contiguous.
+ *   lse             float32 [tokens, q_heads], natural-log log-sum-exp of the
+ *                   scaled logits; optional (NULL skips it).
+ *   dtype           storage type of q, pools, new rows and out; accumulation
+ *                   is always float32.
+ * Grouped-query mapping: q head h reads kv head h / (q_heads / kv_heads).
+ * Causal mask: the query at position p sees keys 0..p.
+ *
+ * Preconditions on device-array contents are not checked by the compute calls
+ * (checking them would need a host synchronisation); msgl_validate_batch
+ * checks host copies.  Only host scalars and pointer presence are validated;
+ * a bad value returns a status and enqueues nothing.
+ *
+ * Supported: dtype F32 or BF16; head_dim 64 or 128; q_heads / kv_heads in
+ * {1, 2, 4, 8}; kv_heads <= 64; page_size >= 1.  Others return
+ * MSGL_UNSUPPORTED.  Thread-safety: calls may be made from several threads;
+ * msgl_last_error is per thread.
+ */
+#ifndef MSGL_H
+#define MSGL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MSGL_OK = 0,
+    MSGL_INVALID_ARG = 1,          /* NULL pointer, negative size, inconsistent scalars */
+    MSGL_UNSUPPORTED = 2,          /* valid but not implemented (dtype, head_dim, group) */
+    MSGL_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the *_workspace_bytes query */
+    MSGL_HIP_ERROR = 4             /* a HIP runtime call or launch failed */
+} msgl_status;
+
+typedef enum { MSGL_F32 = 0, MSGL_BF16 = 1 } msgl_dtype;
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char *msgl_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int msgl_version(void);
+
+/*
+ * msgl_store_kv - write the step's new K/V rows into the pools.
+ * For t in [0, num_tokens): k_pool[out_loc[t]] = k_new[t] and
+ * v_pool[out_loc[t]] = v_new[t], each a [kv_heads, head_dim] row, copied bit
+ * for bit.  This is the KV-write custom kernel of the Stage 4 milestone's
+ * table; it runs before attention in the layer.
+ * out_loc entries must lie in [0, num_slots) and be distinct, except the
+ * dummy request's slot, which padded rows may share (its contents are then
+ * unspecified).  num_tokens == 0 is a no-op.
+ */
+msgl_status msgl_store_kv(void *k_pool, void *v_pool, int64_t num_slots, int32_t kv_heads,
+                          int32_t head_dim, msgl_dtype dtype, const void *k_new,
+                          const void *v_new, const int32_t *out_loc, int32_t num_tokens,
+                          void *stream);
+
+/*
+ * Decode attention: one query token per request, at position seq_lens[b] - 1
+ * (the token just written by msgl_store_kv, so a request attends to itself).
+ * The keys of request b are page_table[table_idx[b], 0 .. seq_lens[b]-1].
+ *
+ * The work is split along the key axis into chunks of `chunk` tokens
+ * (a multiple of 64; 0 picks the library default), and the chunks' partial
+ * softmax states are merged afterwards; the result does not depend on the
+ * chunk size beyond float32 rounding.  max_seq_len bounds every seq_lens[b]
+ * and sizes the workspace; it may exceed the actual lengths (a graph captured
+ * once serves any batch whose lengths stay within it).
+ *
+ * msgl_decode_workspace_bytes returns the workspace size for these scalars.
+ * seq_lens[b] must lie in [1, min(max_seq_len, row_stride)].
+ */
+size_t msgl_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim,
+                                   int32_t max_seq_len, int32_t chunk);
+
+msgl_status msgl_decode_attn(void *out, float *lse, const void *q, const void *k_pool,
+                             const void *v_pool, int64_t num_slots, const int32_t *page_table,
+                             int32_t row_stride, const int32_t *table_idx,
+                             const int32_t *seq_lens, int32_t batch, int32_t q_heads,
+                             int32_t kv_heads, int32_t head_dim, int32_t page_size,
+                             int32_t max_seq_len, int32_t chunk, float sm_scale,
+                             msgl_dtype dtype, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * Prefill / extend attention over a cached prefix (ragged batch).
+ * Request b has seq_lens[b] tokens of which the first cached_lens[b] are
+ * already in the pool from earlier steps; its new tokens are q rows
+ * cu_q[b] .. cu_q[b+1]-1 at positions cached_lens[b] .. seq_lens[b]-1, and
+ * each sees the keys at positions 0..its own position (the causal mask is
+ * offset by the cached length).  Requires
+ * cu_q[b+1] - cu_q[b] == seq_lens[b] - cached_lens[b] >= 1, cu_q[0] == 0,
+ * cu_q[batch] == total_q, and max_extend >= every extend length (it sizes
+ * the grid).  bf16 runs on matrix cores (MFMA); fp32 runs on the vector ALUs.
+ * The prefill call needs no workspace.
+ */
+msgl_status msgl_prefill_attn(void *out, float *lse, const void *q, const void *k_pool,
+                              const void *v_pool, int64_t num_slots, const int32_t *page_table,
+                              int32_t row_stride, const int32_t *table_idx,
+                              const int32_t *seq_lens, const int32_t *cached_lens,
+                              const int32_t *cu_q, int32_t batch, int32_t total_q,
+                              int32_t max_extend, int32_t q_heads, int32_t kv_heads,
+                              int32_t head_dim, int32_t page_size, float sm_scale,
+                              msgl_dtype dtype, void *stream);
+
+/*
+ * Decode step as a captured HIP graph (store_kv, then decode attention), for
+ * one padded batch size, after the CUDA-Graph runner of the Stage 4 milestone:
+ * every input lives in a fixed buffer whose address is recorded at capture;
+ * before each replay the caller writes the step's values into those buffers
+ * (rows beyond the real batch use the dummy request: seq_len 1, table row =
+ * the dummy row, out_loc = the dummy slot) and launches.  The buffers must
+ * stay allocated, at the same addresses, for the graph's lifetime.
+ * `stream` must not be the null stream (capture needs a real stream).
+ * Arguments mean what they mean in msgl_store_kv and msgl_decode_attn with
+ * num_tokens == batch == padded_batch.
+ */
+typedef struct msgl_graph msgl_graph;
+
+msgl_status msgl_decode_graph_create(msgl_graph **graph, void *k_pool, void *v_pool,
+                                     int64_t num_slots, const void *k_new, const void *v_new,
+                                     const int32_t *out_loc, void *out, float *lse,
+                                     const void *q, const int32_t *page_table,
+                                     int32_t row_stride, const int32_t *table_idx,
+                                     const int32_t *seq_lens, int32_t padded_batch,
+                                     int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                     int32_t page_size, int32_t max_seq_len, int32_t chunk,
+                                     float sm_scale, msgl_dtype dtype, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/* Enqueue one replay of the captured step on `stream`. */
+msgl_status msgl_graph_launch(msgl_graph *graph, void *stream);
+
+/* Release the graph (NULL is ignored).  Does not touch the recorded buffers. */
+void msgl_graph_destroy(msgl_graph *graph);
+
+/*
+ * msgl_validate_batch - check a batch's metadata on HOST copies (no GPU use).
+ * Checks, for b < batch: 0 <= table_idx[b] < rows; 1 <= seq_lens[b] <=
+ * min(max_seq_len, row_stride); 0 <= cached_lens[b] < seq_lens[b]; when cu_q
+ * is given, cu_q[0] == 0 and cu_q[b+1] - cu_q[b] == seq_lens[b] - cached_lens[b];
+ * every page-table entry a request uses lies in [0, num_slots); when
+ * page_size > 1, the entries of each page are consecutive and the page's
+ * first entry is a multiple of page_size; when out_loc is given (num_tokens
+ * entries), out_loc entries lie in [0, num_slots) and no slot other than
+ * `dummy_slot` repeats (pass -1 to allow no repeats).
+ * cached_lens and cu_q may be NULL (decode: cached = seq_len - 1).
+ * Returns MSGL_OK or MSGL_INVALID_ARG with the first violation in
+ * msgl_last_error.
+ */
+msgl_status msgl_validate_batch(const int32_t *page_table, int32_t rows, int32_t row_stride,
+                                const int32_t *table_idx, const int32_t *seq_lens,
+                                const int32_t *cached_lens, const int32_t *cu_q, int32_t batch,
+                                int32_t max_seq_len, int64_t num_slots, int32_t page_size,
+                                const int32_t *out_loc, int32_t num_tokens, int64_t dummy_slot);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSGL_H */

@@ -1,0 +1,362 @@
+// C ABI of libmsgl (declared in include/msgl.h): argument checks, dispatch to
+// the kernel launchers, decode-step graph capture, and the host-side batch
+// validator.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/msgl.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+msgl_status fail(msgl_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+msgl_status ok() { return MSGL_OK; }
+
+msgl_status from_hip(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(MSGL_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(msgl_dtype d) { return d == MSGL_F32 ? 4 : 2; }
+
+msgl_status check_common(msgl_dtype dtype, int32_t head_dim, int32_t kv_heads, int64_t num_slots) {
+    if (dtype != MSGL_F32 && dtype != MSGL_BF16) return fail(MSGL_UNSUPPORTED, "dtype %d not supported", (int)dtype);
+    if (head_dim != 64 && head_dim != 128) return fail(MSGL_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+    if (kv_heads < 1 || kv_heads > 64) return fail(kv_heads < 1 ? MSGL_INVALID_ARG : MSGL_UNSUPPORTED, "kv_heads %d out of range [1, 64]", kv_heads);
+    if (num_slots < 1) return fail(MSGL_INVALID_ARG, "num_slots %lld < 1", (long long)num_slots);
+    return ok();
+}
+
+msgl_status check_group(int32_t q_heads, int32_t kv_heads) {
+    if (q_heads < 1 || q_heads % kv_heads != 0)
+        return fail(MSGL_INVALID_ARG, "q_heads %d is not a multiple of kv_heads %d", q_heads, kv_heads);
+    const int g = q_heads / kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8)
+        return fail(MSGL_UNSUPPORTED, "group size q_heads/kv_heads = %d not in {1, 2, 4, 8}", g);
+    return ok();
+}
+
+constexpr int32_t kMaxDecodeBatch = 8192;
+
+int32_t effective_chunk(int32_t chunk) { return chunk == 0 ? msgl::kDefaultChunk : chunk; }
+
+msgl_status check_decode(const void *out, const void *q, const void *k_pool, const void *v_pool,
+                         int64_t num_slots, const int32_t *page_table, int32_t row_stride,
+                         const int32_t *table_idx, const int32_t *seq_lens, int32_t batch,
+                         int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t page_size,
+                         int32_t max_seq_len, int32_t chunk, msgl_dtype dtype, const void *workspace,
+                         size_t workspace_bytes) {
+    msgl_status s = check_common(dtype, head_dim, kv_heads, num_slots);
+    if (s != MSGL_OK) return s;
+    if ((s = check_group(q_heads, kv_heads)) != MSGL_OK) return s;
+    if (batch < 0 || batch > kMaxDecodeBatch)
+        return fail(batch < 0 ? MSGL_INVALID_ARG : MSGL_UNSUPPORTED, "batch %d out of range [0, %d]", batch, kMaxDecodeBatch);
+    if (batch > 0 && (!out || !q || !k_pool || !v_pool || !page_table || !table_idx || !seq_lens || !workspace))
+        return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    if (row_stride < 1) return fail(MSGL_INVALID_ARG, "row_stride %d < 1", row_stride);
+    if (max_seq_len < 1 || max_seq_len > row_stride)
+        return fail(MSGL_INVALID_ARG, "max_seq_len %d not in [1, row_stride=%d]", max_seq_len, row_stride);
+    if (page_size < 1) return fail(MSGL_INVALID_ARG, "page_size %d < 1", page_size);
+    const int32_t c = effective_chunk(chunk);
+    if (c < 64 || c % 64 != 0) return fail(MSGL_INVALID_ARG, "chunk %d is not a positive multiple of 64", chunk);
+    const size_t need = msgl::decode_workspace_bytes(batch, q_heads, head_dim, max_seq_len, c);
+    if (workspace_bytes < need)
+        return fail(MSGL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    return ok();
+}
+
+msgl::DecodeArgs decode_args(void *out, float *lse, const void *q, const void *k_pool,
+                             const void *v_pool, int64_t num_slots, const int32_t *page_table,
+                             int32_t row_stride,
+                             const int32_t *table_idx, const int32_t *seq_lens, int32_t batch,
+                             int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                             int32_t max_seq_len, int32_t chunk, float sm_scale, void *workspace) {
+    msgl::DecodeArgs a;
+    const int32_t c = effective_chunk(chunk);
+    a.out = out;
+    a.lse = lse;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.page_table = page_table;
+    a.row_stride = row_stride;
+    a.table_idx = table_idx;
+    a.seq_lens = seq_lens;
+    a.num_slots = num_slots;
+    a.batch = batch;
+    a.q_heads = q_heads;
+    a.kv_heads = kv_heads;
+    a.chunk = c;
+    a.max_splits = (max_seq_len + c - 1) / c;
+    a.scale_log2 = sm_scale * msgl::kLog2eHost;
+    char *ws = static_cast<char *>(workspace);
+    a.ctrl = reinterpret_cast<uint32_t *>(ws);
+    const size_t parts = (size_t)batch * a.max_splits * q_heads;
+    a.part_o = reinterpret_cast<float *>(ws + msgl::kCtrlBytes);
+    a.part_ml = a.part_o + parts * head_dim;
+    return a;
+}
+
+msgl_status check_store(void *k_pool, void *v_pool, int64_t num_slots, int32_t kv_heads,
+                        int32_t head_dim, msgl_dtype dtype, const void *k_new, const void *v_new,
+                        const int32_t *out_loc, int32_t num_tokens) {
+    msgl_status s = check_common(dtype, head_dim, kv_heads, num_slots);
+    if (s != MSGL_OK) return s;
+    if (num_tokens < 0) return fail(MSGL_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+    if (num_tokens > 0 && (!k_pool || !v_pool || !k_new || !v_new || !out_loc))
+        return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    return ok();
+}
+
+msgl::StoreKvArgs store_args(void *k_pool, void *v_pool, int64_t num_slots, int32_t kv_heads,
+                             int32_t head_dim,
+                             msgl_dtype dtype, const void *k_new, const void *v_new,
+                             const int32_t *out_loc, int32_t num_tokens) {
+    msgl::StoreKvArgs a;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.out_loc = out_loc;
+    a.num_tokens = num_tokens;
+    a.row_vec16 = kv_heads * head_dim * elem_bytes(dtype) / 16;
+    a.num_slots = num_slots;
+    return a;
+}
+
+}  // namespace
+
+struct msgl_graph {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+const char *msgl_last_error(void) { return g_err.c_str(); }
+
+int msgl_version(void) { return 100; }
+
+msgl_status msgl_store_kv(void *k_pool, void *v_pool, int64_t num_slots, int32_t kv_heads,
+                          int32_t head_dim, msgl_dtype dtype, const void *k_new,
+                          const void *v_new, const int32_t *out_loc, int32_t num_tokens,
+                          void *stream) {
+    msgl_status s = check_store(k_pool, v_pool, num_slots, kv_heads, head_dim, dtype, k_new, v_new,
+                                out_loc, num_tokens);
+    if (s != MSGL_OK) return s;
+    if (num_tokens == 0) return ok();
+    return from_hip(msgl::launch_store_kv(store_args(k_pool, v_pool, num_slots, kv_heads, head_dim, dtype, k_new,
+                                                     v_new, out_loc, num_tokens),
+                                          static_cast<hipStream_t>(stream)),
+                    "store_kv launch");
+}
+
+size_t msgl_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim,
+                                   int32_t max_seq_len, int32_t chunk) {
+    if (batch < 0 || q_heads < 1 || head_dim < 1 || max_seq_len < 1) return 0;
+    return msgl::decode_workspace_bytes(batch, q_heads, head_dim, max_seq_len, effective_chunk(chunk));
+}
+
+msgl_status msgl_decode_attn(void *out, float *lse, const void *q, const void *k_pool,
+                             const void *v_pool, int64_t num_slots, const int32_t *page_table,
+                             int32_t row_stride, const int32_t *table_idx,
+                             const int32_t *seq_lens, int32_t batch, int32_t q_heads,
+                             int32_t kv_heads, int32_t head_dim, int32_t page_size,
+                             int32_t max_seq_len, int32_t chunk, float sm_scale,
+                             msgl_dtype dtype, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    msgl_status s = check_decode(out, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx,
+                                 seq_lens, batch, q_heads, kv_heads, head_dim, page_size, max_seq_len,
+                                 chunk, dtype, workspace, workspace_bytes);
+    if (s != MSGL_OK) return s;
+    if (batch == 0) return ok();
+    msgl::DecodeArgs a = decode_args(out, lse, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx,
+                                     seq_lens, batch, q_heads, kv_heads, head_dim, max_seq_len, chunk,
+                                     sm_scale, workspace);
+    return from_hip(msgl::launch_decode(a, static_cast<msgl::DType>(dtype), head_dim,
+                                        static_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
+msgl_status msgl_prefill_attn(void *out, float *lse, const void *q, const void *k_pool,
+                              const void *v_pool, int64_t num_slots, const int32_t *page_table,
+                              int32_t row_stride, const int32_t *table_idx,
+                              const int32_t *seq_lens, const int32_t *cached_lens,
+                              const int32_t *cu_q, int32_t batch, int32_t total_q,
+                              int32_t max_extend, int32_t q_heads, int32_t kv_heads,
+                              int32_t head_dim, int32_t page_size, float sm_scale,
+                              msgl_dtype dtype, void *stream) {
+    msgl_status s = check_common(dtype, head_dim, kv_heads, num_slots);
+    if (s != MSGL_OK) return s;
+    if ((s = check_group(q_heads, kv_heads)) != MSGL_OK) return s;
+    if (batch < 0 || total_q < 0) return fail(MSGL_INVALID_ARG, "negative batch or total_q");
+    if (batch == 0 || total_q == 0) {
+        if (batch == 0 && total_q == 0) return ok();
+        return fail(MSGL_INVALID_ARG, "batch %d and total_q %d must both be zero or both positive", batch, total_q);
+    }
+    if (total_q < batch) return fail(MSGL_INVALID_ARG, "total_q %d < batch %d (each request needs a new token)", total_q, batch);
+    if (max_extend < 1 || max_extend > total_q)
+        return fail(MSGL_INVALID_ARG, "max_extend %d not in [1, total_q=%d]", max_extend, total_q);
+    if (!out || !q || !k_pool || !v_pool || !page_table || !table_idx || !seq_lens || !cached_lens || !cu_q)
+        return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    if (row_stride < 1) return fail(MSGL_INVALID_ARG, "row_stride %d < 1", row_stride);
+    if (page_size < 1) return fail(MSGL_INVALID_ARG, "page_size %d < 1", page_size);
+    msgl::PrefillArgs a;
+    a.out = out;
+    a.lse = lse;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.page_table = page_table;
+    a.row_stride = row_stride;
+    a.table_idx = table_idx;
+    a.seq_lens = seq_lens;
+    a.cached_lens = cached_lens;
+    a.cu_q = cu_q;
+    a.num_slots = num_slots;
+    a.batch = batch;
+    a.total_q = total_q;
+    a.max_extend = max_extend;
+    a.q_heads = q_heads;
+    a.kv_heads = kv_heads;
+    a.scale_log2 = sm_scale * msgl::kLog2eHost;
+    return from_hip(msgl::launch_prefill(a, static_cast<msgl::DType>(dtype), head_dim,
+                                         static_cast<hipStream_t>(stream)),
+                    "prefill launch");
+}
+
+msgl_status msgl_decode_graph_create(msgl_graph **graph, void *k_pool, void *v_pool,
+                                     int64_t num_slots, const void *k_new, const void *v_new,
+                                     const int32_t *out_loc, void *out, float *lse,
+                                     const void *q, const int32_t *page_table,
+                                     int32_t row_stride, const int32_t *table_idx,
+                                     const int32_t *seq_lens, int32_t padded_batch,
+                                     int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                     int32_t page_size, int32_t max_seq_len, int32_t chunk,
+                                     float sm_scale, msgl_dtype dtype, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    if (!graph) return fail(MSGL_INVALID_ARG, "NULL graph handle pointer");
+    *graph = nullptr;
+    if (!stream) return fail(MSGL_INVALID_ARG, "graph capture needs a non-null stream");
+    if (padded_batch < 1) return fail(MSGL_INVALID_ARG, "padded_batch %d < 1", padded_batch);
+    msgl_status s = check_store(k_pool, v_pool, num_slots, kv_heads, head_dim, dtype, k_new, v_new,
+                                out_loc, padded_batch);
+    if (s != MSGL_OK) return s;
+    s = check_decode(out, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx, seq_lens,
+                     padded_batch, q_heads, kv_heads, head_dim, page_size, max_seq_len, chunk, dtype,
+                     workspace, workspace_bytes);
+    if (s != MSGL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    msgl::StoreKvArgs sa = store_args(k_pool, v_pool, num_slots, kv_heads, head_dim, dtype, k_new, v_new, out_loc,
+                                      padded_batch);
+    msgl::DecodeArgs da = decode_args(out, lse, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx,
+                                      seq_lens, padded_batch, q_heads, kv_heads, head_dim, max_seq_len,
+                                      chunk, sm_scale, workspace);
+    hipError_t e = msgl::launch_decode(da, static_cast<msgl::DType>(dtype), head_dim, st, true);
+    if (e != hipSuccess) return from_hip(e, "decode preparation");
+    e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return from_hip(e, "hipStreamBeginCapture");
+    hipError_t e1 = msgl::launch_store_kv(sa, st);
+    hipError_t e2 = e1 == hipSuccess ? msgl::launch_decode(da, static_cast<msgl::DType>(dtype), head_dim, st)
+                                     : hipSuccess;
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(st, &g);
+    if (e1 != hipSuccess || e2 != hipSuccess || e != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        return from_hip(e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e), "decode graph capture");
+    }
+    hipGraphExec_t ex = nullptr;
+    e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        return from_hip(e, "hipGraphInstantiate");
+    }
+    msgl_graph *h = new (std::nothrow) msgl_graph;
+    if (!h) {
+        (void)hipGraphExecDestroy(ex);
+        (void)hipGraphDestroy(g);
+        return fail(MSGL_INVALID_ARG, "out of host memory");
+    }
+    h->graph = g;
+    h->exec = ex;
+    *graph = h;
+    return ok();
+}
+
+msgl_status msgl_graph_launch(msgl_graph *graph, void *stream) {
+    if (!graph || !graph->exec) return fail(MSGL_INVALID_ARG, "NULL graph");
+    return from_hip(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)), "hipGraphLaunch");
+}
+
+void msgl_graph_destroy(msgl_graph *graph) {
+    if (!graph) return;
+    if (graph->exec) (void)hipGraphExecDestroy(graph->exec);
+    if (graph->graph) (void)hipGraphDestroy(graph->graph);
+    delete graph;
+}
+
+msgl_status msgl_validate_batch(const int32_t *page_table, int32_t rows, int32_t row_stride,
+                                const int32_t *table_idx, const int32_t *seq_lens,
+                                const int32_t *cached_lens, const int32_t *cu_q, int32_t batch,
+                                int32_t max_seq_len, int64_t num_slots, int32_t page_size,
+                                const int32_t *out_loc, int32_t num_tokens, int64_t dummy_slot) {
+    if (!page_table || !table_idx || !seq_lens) return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    if (rows < 1 || row_stride < 1 || batch < 0 || num_slots < 1 || page_size < 1 || num_tokens < 0)
+        return fail(MSGL_INVALID_ARG, "bad scalar argument");
+    const int32_t lim = max_seq_len < row_stride ? max_seq_len : row_stride;
+    if (cu_q && cu_q[0] != 0) return fail(MSGL_INVALID_ARG, "cu_q[0] = %d, expected 0", cu_q[0]);
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t r = table_idx[b];
+        if (r < 0 || r >= rows) return fail(MSGL_INVALID_ARG, "table_idx[%d] = %d outside [0, %d)", b, r, rows);
+        const int32_t L = seq_lens[b];
+        if (L < 1 || L > lim) return fail(MSGL_INVALID_ARG, "seq_lens[%d] = %d outside [1, %d]", b, L, lim);
+        const int32_t C = cached_lens ? cached_lens[b] : L - 1;
+        if (C < 0 || C >= L) return fail(MSGL_INVALID_ARG, "cached_lens[%d] = %d outside [0, %d)", b, C, L);
+        if (cu_q && cu_q[b + 1] - cu_q[b] != L - C)
+            return fail(MSGL_INVALID_ARG, "cu_q[%d+1] - cu_q[%d] = %d, expected seq_len - cached_len = %d", b, b,
+                        cu_q[b + 1] - cu_q[b], L - C);
+        const int32_t *row = page_table + (int64_t)r * row_stride;
+        for (int32_t j = 0; j < L; ++j) {
+            if (row[j] < 0 || row[j] >= num_slots)
+                return fail(MSGL_INVALID_ARG, "page_table[%d, %d] = %d outside [0, %lld)", r, j, row[j],
+                            (long long)num_slots);
+            if (page_size > 1) {
+                const int32_t off = j % page_size;
+                if (off == 0 && row[j] % page_size != 0)
+                    return fail(MSGL_INVALID_ARG, "page_table[%d, %d] = %d does not start a page", r, j, row[j]);
+                if (off != 0 && row[j] != row[j - 1] + 1)
+                    return fail(MSGL_INVALID_ARG, "page_table[%d, %d] breaks page contiguity", r, j);
+            }
+        }
+    }
+    if (out_loc) {
+        std::vector<unsigned char> seen((size_t)num_slots, 0);
+        for (int32_t t = 0; t < num_tokens; ++t) {
+            const int32_t s = out_loc[t];
+            if (s < 0 || s >= num_slots)
+                return fail(MSGL_INVALID_ARG, "out_loc[%d] = %d outside [0, %lld)", t, s, (long long)num_slots);
+            if (seen[(size_t)s] && s != dummy_slot)
+                return fail(MSGL_INVALID_ARG, "out_loc[%d] = %d repeats a slot", t, s);
+            seen[(size_t)s] = 1;
+        }
+    }
+    return ok();
+}
+
+}  // extern "C"

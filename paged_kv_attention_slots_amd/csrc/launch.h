@@ -1,0 +1,84 @@
+// Host-side launchers of the msgl kernels (internal; the C ABI is include/msgl.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msgl {
+
+enum DType { kF32 = 0, kBF16 = 1 };
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Decode split size used when the caller passes chunk == 0.
+constexpr int kDefaultChunk = 256;
+// Bytes of the decode workspace's control block (work-queue counters).
+constexpr size_t kCtrlBytes = 256;
+
+struct StoreKvArgs {
+    void *k_pool;
+    void *v_pool;
+    const void *k_new;
+    const void *v_new;
+    const int32_t *out_loc;
+    int32_t num_tokens;
+    int32_t row_vec16;  // 16-byte vectors per [kv_heads, head_dim] row
+    int64_t num_slots;  // rows with an out_loc outside [0, num_slots) are skipped
+};
+
+struct DecodeArgs {
+    void *out;
+    float *lse;
+    const void *q;
+    const void *k_pool;
+    const void *v_pool;
+    const int32_t *page_table;
+    int64_t row_stride;
+    const int32_t *table_idx;
+    const int32_t *seq_lens;
+    int64_t num_slots;  // slot ids outside [0, num_slots) read slot 0 instead
+    int32_t batch;
+    int32_t q_heads;
+    int32_t kv_heads;
+    int32_t chunk;
+    int32_t max_splits;
+    float scale_log2;  // sm_scale * log2(e)
+    float *part_o;     // [batch, max_splits, q_heads, head_dim]
+    float *part_ml;    // [batch, max_splits, q_heads, 2]  (max in log2 units, sum)
+    uint32_t *ctrl;    // [2] work-queue counter, finished-group counter (zero between calls)
+};
+
+struct PrefillArgs {
+    void *out;
+    float *lse;
+    const void *q;
+    const void *k_pool;
+    const void *v_pool;
+    const int32_t *page_table;
+    int64_t row_stride;
+    const int32_t *table_idx;
+    const int32_t *seq_lens;
+    const int32_t *cached_lens;
+    const int32_t *cu_q;
+    int64_t num_slots;
+    int32_t batch;
+    int32_t total_q;
+    int32_t max_extend;
+    int32_t q_heads;
+    int32_t kv_heads;
+    float scale_log2;
+};
+
+size_t decode_workspace_bytes(int batch, int q_heads, int head_dim, int max_seq_len, int chunk);
+
+hipError_t launch_store_kv(const StoreKvArgs &a, hipStream_t stream);
+// prepare_only resolves the cached device queries and launches nothing (call
+// it before capturing the launch into a graph).
+hipError_t launch_decode(const DecodeArgs &a, DType dtype, int head_dim, hipStream_t stream,
+                         bool prepare_only = false);
+// bf16 prefill on matrix cores when the shape is supported, else the VALU path.
+hipError_t launch_prefill(const PrefillArgs &a, DType dtype, int head_dim, hipStream_t stream);
+hipError_t launch_prefill_valu(const PrefillArgs &a, DType dtype, int head_dim, hipStream_t stream);
+
+}  // namespace msgl

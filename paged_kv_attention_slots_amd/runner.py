@@ -1,0 +1,67 @@
+"""Drive one attention step of a workload through the C ABI.
+
+Plumbing only: allocate outputs and workspaces with torch on the workload's
+device and call the binding.  All computation happens in libmsgl's kernels.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+from .workloads import Workload
+
+
+@dataclasses.dataclass
+class StepResult:
+    out: torch.Tensor
+    lse: Optional[torch.Tensor]
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+
+
+def store_kv(w: Workload, k_pool: torch.Tensor, v_pool: torch.Tensor, stream=None) -> None:
+    _lib.msgl_store_kv(k_pool, v_pool, w.k_new, w.v_new, w.out_loc, stream=stream)
+
+
+def decode_attn(w: Workload, k_pool, v_pool, out=None, lse=None, workspace=None, chunk: int = 0,
+                with_lse: bool = True, stream=None):
+    dev = w.q.device
+    if out is None:
+        out = torch.empty_like(w.q)
+    if lse is None and with_lse:
+        lse = torch.empty(w.bs, w.q_heads, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _lib.decode_workspace(w.bs, w.q_heads, w.head_dim, w.max_seq_len, chunk, device=dev)
+    _lib.msgl_decode_attn(out, lse, w.q, k_pool, v_pool, w.page_table, w.table_idx, w.seq_lens,
+                          w.max_seq_len, workspace, page_size=w.page_size, chunk=chunk,
+                          sm_scale=w.sm_scale, stream=stream)
+    return out, lse
+
+
+def prefill_attn(w: Workload, k_pool, v_pool, out=None, lse=None, with_lse: bool = True, stream=None):
+    dev = w.q.device
+    if out is None:
+        out = torch.empty_like(w.q)
+    if lse is None and with_lse:
+        lse = torch.empty(w.num_tokens, w.q_heads, dtype=torch.float32, device=dev)
+    max_extend = int((w.seq_lens - w.cached_lens).max().item())
+    _lib.msgl_prefill_attn(out, lse, w.q, k_pool, v_pool, w.page_table, w.table_idx, w.seq_lens,
+                           w.cached_lens, w.cu_q, max_extend, page_size=w.page_size,
+                           sm_scale=w.sm_scale, stream=stream)
+    return out, lse
+
+
+def run_step(w: Workload, chunk: int = 0, with_lse: bool = True, in_place: bool = False) -> StepResult:
+    """store_kv then attention (decode or prefill by the workload's mode)."""
+    kp = w.k_pool if in_place else w.k_pool.clone()
+    vp = w.v_pool if in_place else w.v_pool.clone()
+    store_kv(w, kp, vp)
+    if w.mode == "decode":
+        out, lse = decode_attn(w, kp, vp, chunk=chunk, with_lse=with_lse)
+    else:
+        out, lse = prefill_attn(w, kp, vp, with_lse=with_lse)
+    return StepResult(out, lse, kp, vp)

@@ -1,0 +1,171 @@
+"""The C ABI library loads and exports every declared symbol, and its host-side
+logic (argument checks, status codes, the batch validator) works without a GPU.
+No call here reaches a kernel launch: every compute call below fails its
+argument checks first."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msgl.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(msgl_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from paged_kv_attention_slots_amd import _lib
+
+    return _lib
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 10
+    assert set(names) == set(L.EXPORTS)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_error_text(L):
+    assert L.msgl_version() >= 100
+    assert isinstance(L.msgl_last_error(), str)
+
+
+FAKE = 0x10000  # never dereferenced: every call below is rejected before launch
+
+
+def test_store_kv_argument_checks(L):
+    lib = L.lib
+    st = lib.msgl_store_kv(FAKE, FAKE, 100, 8, 96, 1, FAKE, FAKE, FAKE, 4, None)
+    assert st == L.MSGL_UNSUPPORTED and "head_dim" in L.msgl_last_error()
+    st = lib.msgl_store_kv(FAKE, FAKE, 100, 8, 128, 7, FAKE, FAKE, FAKE, 4, None)
+    assert st == L.MSGL_UNSUPPORTED
+    st = lib.msgl_store_kv(None, FAKE, 100, 8, 128, 1, FAKE, FAKE, FAKE, 4, None)
+    assert st == L.MSGL_INVALID_ARG
+    st = lib.msgl_store_kv(FAKE, FAKE, 100, 8, 128, 1, FAKE, FAKE, FAKE, -1, None)
+    assert st == L.MSGL_INVALID_ARG
+    st = lib.msgl_store_kv(FAKE, FAKE, 0, 8, 128, 1, FAKE, FAKE, FAKE, 1, None)
+    assert st == L.MSGL_INVALID_ARG
+    # zero tokens is a no-op that needs no pointers and no GPU
+    assert lib.msgl_store_kv(None, None, 100, 8, 128, 1, None, None, None, 0, None) == L.MSGL_OK
+
+
+def _decode(L, **over):
+    a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, S=1000, pt=FAKE, W=4096, tix=FAKE, sl=FAKE,
+             bs=4, H=32, G=8, d=128, ps=1, msl=4096, chunk=0, scale=0.088, dt=1, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return L.lib.msgl_decode_attn(a["out"], a["lse"], a["q"], a["k"], a["v"], a["S"], a["pt"], a["W"],
+                                  a["tix"], a["sl"], a["bs"], a["H"], a["G"], a["d"], a["ps"], a["msl"],
+                                  a["chunk"], a["scale"], a["dt"], a["ws"], a["wsb"], None)
+
+
+def test_decode_argument_checks(L):
+    assert _decode(L, H=12) == L.MSGL_INVALID_ARG  # not a multiple of kv_heads
+    assert _decode(L, H=30) == L.MSGL_INVALID_ARG
+    assert _decode(L, H=8 * 16) == L.MSGL_UNSUPPORTED  # group 16
+    assert _decode(L, d=80) == L.MSGL_UNSUPPORTED
+    assert _decode(L, q=None) == L.MSGL_INVALID_ARG
+    assert _decode(L, msl=5000) == L.MSGL_INVALID_ARG  # beyond row_stride
+    assert _decode(L, chunk=100) == L.MSGL_INVALID_ARG
+    assert _decode(L, ps=0) == L.MSGL_INVALID_ARG
+    need = L.msgl_decode_workspace_bytes(4, 32, 128, 4096)
+    assert need > 0
+    assert _decode(L, wsb=need - 1) == L.MSGL_WORKSPACE_TOO_SMALL
+    assert "workspace" in L.msgl_last_error()
+    assert _decode(L, bs=-1) == L.MSGL_INVALID_ARG
+    assert _decode(L, bs=100000) == L.MSGL_UNSUPPORTED
+
+
+def test_decode_workspace_size_formula(L):
+    # control block + (m, l, o[d]) float32 per (request, chunk, q head)
+    bs, H, d, msl, chunk = 256, 32, 128, 32768, 256
+    splits = (msl + chunk - 1) // chunk
+    assert L.msgl_decode_workspace_bytes(bs, H, d, msl, chunk) == 256 + bs * splits * H * (d + 2) * 4
+    assert L.msgl_decode_workspace_bytes(bs, H, d, msl, 0) == L.msgl_decode_workspace_bytes(bs, H, d, msl, 256)
+
+
+def _prefill(L, **over):
+    a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, S=1000, pt=FAKE, W=4096, tix=FAKE, sl=FAKE,
+             cl=FAKE, cu=FAKE, bs=2, T=10, me=8, H=16, G=8, d=128, ps=1, scale=0.088, dt=1)
+    a.update(over)
+    return L.lib.msgl_prefill_attn(a["out"], a["lse"], a["q"], a["k"], a["v"], a["S"], a["pt"], a["W"],
+                                   a["tix"], a["sl"], a["cl"], a["cu"], a["bs"], a["T"], a["me"], a["H"],
+                                   a["G"], a["d"], a["ps"], a["scale"], a["dt"], None)
+
+
+def test_prefill_argument_checks(L):
+    assert _prefill(L, T=1) == L.MSGL_INVALID_ARG   # fewer tokens than requests
+    assert _prefill(L, me=0) == L.MSGL_INVALID_ARG
+    assert _prefill(L, me=11) == L.MSGL_INVALID_ARG
+    assert _prefill(L, cl=None) == L.MSGL_INVALID_ARG
+    assert _prefill(L, bs=0, T=3) == L.MSGL_INVALID_ARG
+    assert _prefill(L, bs=0, T=0) == L.MSGL_OK
+    assert _prefill(L, G=3) == L.MSGL_INVALID_ARG
+
+
+def test_graph_handle_checks(L):
+    lib = L.lib
+    assert lib.msgl_graph_launch(None, None) == L.MSGL_INVALID_ARG
+    lib.msgl_graph_destroy(None)
+    h = ctypes.c_void_p()
+    st = lib.msgl_decode_graph_create(ctypes.byref(h), FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                      FAKE, 64, FAKE, FAKE, 4, 32, 8, 128, 1, 64, 0, 0.1, 1, FAKE, 1 << 20,
+                                      None)
+    assert st == L.MSGL_INVALID_ARG and "stream" in L.msgl_last_error()
+
+
+def test_validate_batch(L):
+    from paged_kv_attention_slots_amd import workloads as wl
+
+    w = wl.qwen3_8b_decode(page_size=16, bs=5, num_slots=1 << 12, median=100.0, hi=512)
+    args = dict(max_seq_len=w.max_seq_len, num_slots=w.num_slots_total, page_size=16)
+    L.msgl_validate_batch(w.page_table, w.table_idx, w.seq_lens, w.cached_lens, w.cu_q,
+                          out_loc=w.out_loc, dummy_slot=w.dummy_slot, **args)
+    p = wl.pad_decode(w, 8)
+    L.msgl_validate_batch(p.page_table, p.table_idx, p.seq_lens, p.cached_lens, p.cu_q,
+                          out_loc=p.out_loc, dummy_slot=w.dummy_slot, **args)
+    with pytest.raises(L.MsglError):  # repeated dummy slot not allowed without naming it
+        L.msgl_validate_batch(p.page_table, p.table_idx, p.seq_lens, p.cached_lens, p.cu_q,
+                              out_loc=p.out_loc, dummy_slot=-1, **args)
+    bad = w.page_table.clone()
+    bad[0, 3] += 1  # breaks page contiguity
+    with pytest.raises(L.MsglError, match="contiguity"):
+        L.msgl_validate_batch(bad, w.table_idx, w.seq_lens, w.cached_lens, w.cu_q, **args)
+    sl = w.seq_lens.clone()
+    sl[1] = 0
+    with pytest.raises(L.MsglError, match="seq_lens"):
+        L.msgl_validate_batch(w.page_table, w.table_idx, sl, None, None, **args)
+    cu = w.cu_q.clone()
+    cu[2] += 1
+    with pytest.raises(L.MsglError, match="cu_q"):
+        L.msgl_validate_batch(w.page_table, w.table_idx, w.seq_lens, w.cached_lens, cu, **args)
+    loc = w.out_loc.clone()
+    loc[0] = w.num_slots_total
+    with pytest.raises(L.MsglError, match="out_loc"):
+        L.msgl_validate_batch(w.page_table, w.table_idx, w.seq_lens, w.cached_lens, w.cu_q,
+                              out_loc=loc, **args)
+    tix = w.table_idx.clone()
+    tix[0] = 99
+    with pytest.raises(L.MsglError, match="table_idx"):
+        L.msgl_validate_batch(w.page_table, tix, w.seq_lens, None, None, **args)
+    pt = w.page_table.clone()
+    pt[2, 0] = -5
+    with pytest.raises(L.MsglError, match="page_table"):
+        L.msgl_validate_batch(pt, w.table_idx, w.seq_lens, None, None, max_seq_len=w.max_seq_len,
+                              num_slots=w.num_slots_total, page_size=1)
+
+
+def test_binding_refuses_host_tensors(L):
+    x = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        L.msgl_store_kv(x, x, x[:1], x[:1], torch.zeros(1, dtype=torch.int32))
