@@ -41,10 +41,10 @@ class MsglError(RuntimeError):
         self.status = status
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run paged_kv_attention_slots_amd.build.build()")
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run paged_kv_attention_slots_amd.build.build()")
+    lib = ctypes.CDLL(path)
     P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     st = ctypes.c_int
     lib.msgl_last_error.restype = ctypes.c_char_p

@@ -103,13 +103,14 @@ msgl::DecodeArgs decode_args(void *out, float *lse, const void *q, const void *k
     a.q_heads = q_heads;
     a.kv_heads = kv_heads;
     a.chunk = c;
-    a.max_splits = (max_seq_len + c - 1) / c;
+    a.max_seq_len = max_seq_len;
     a.scale_log2 = sm_scale * msgl::kLog2eHost;
     char *ws = static_cast<char *>(workspace);
-    a.ctrl = reinterpret_cast<uint32_t *>(ws);
-    const size_t parts = (size_t)batch * a.max_splits * q_heads;
-    a.part_o = reinterpret_cast<float *>(ws + msgl::kCtrlBytes);
-    a.part_ml = a.part_o + parts * head_dim;
+    a.ctrl = reinterpret_cast<int64_t *>(ws);
+    a.prefix = reinterpret_cast<int32_t *>(ws + msgl::kCtrlBytes);
+    const size_t pieces = (size_t)batch + msgl::kMaxDecodeGrid;
+    a.part_o = reinterpret_cast<float *>(ws + msgl::kCtrlBytes + msgl::decode_prefix_bytes(batch));
+    a.part_ml = a.part_o + pieces * q_heads * head_dim;
     return a;
 }
 

@@ -109,99 +109,141 @@ struct SoftmaxState {
     }
 };
 
+// Page-table ids of one iteration's tokens (base + u*RPW + rg), -1 past te.
+template <int U, int RPW>
+MSGL_DEV void load_slots(int (&slot)[U], const int32_t *__restrict__ pt, int base, int te, int rg) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int tok = base + u * RPW + rg;
+        slot[u] = tok < te ? pt[tok] : -1;
+    }
+}
+
+// Issue the K and V loads of one iteration.  Slot ids outside [0, num_slots)
+// (malformed input) read slot 0, so no access leaves the pools; a -1 slot
+// (past the range) loads nothing.
+template <typename T, int U>
+MSGL_DEV void issue_kv(uint4 (&kv)[U], uint4 (&vv)[U], const int (&slot)[U], const T *__restrict__ kbase,
+                       const T *__restrict__ vbase, int64_t row_elems, uint32_t num_slots) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (slot[u] >= 0) {
+            const int64_t off = (int64_t)((uint32_t)slot[u] < num_slots ? slot[u] : 0) * row_elems;
+            kv[u] = ld16_nt(kbase + off);
+            vv[u] = ld16_nt(vbase + off);
+        } else {
+            kv[u] = make_uint4(0, 0, 0, 0);
+            vv[u] = make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+// Scores, online-softmax update and P.V of one iteration's tokens.
+template <typename T, int D, int GQ, int U>
+MSGL_DEV void consume_iter(const uint4 (&kv)[U], const uint4 (&vv)[U], const int (&slot)[U],
+                           const QSlice<T> (&q)[GQ], float scale_log2, SoftmaxState<T, D, GQ> &st) {
+    constexpr int E = Store<T>::kEpl;
+    constexpr int LPR = Geometry<T, D>::kLpr;
+    float s[U][GQ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            const float d = group_sum<LPR>(q[h].dot(kv[u]));
+            s[u][h] = slot[u] >= 0 ? d * scale_log2 : -INFINITY;
+        }
+    }
+    float p[U][GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+        float mx = s[0][h];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][h]);
+        const float mn = fmaxf(st.m[h], mx);
+        const float mu = (mn == -INFINITY) ? 0.0f : mn;
+        const float alpha = fast_exp2(st.m[h] - mu);
+        float psum = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            p[u][h] = fast_exp2(s[u][h] - mu);
+            psum += p[u][h];
+        }
+        st.l[h] = st.l[h] * alpha + psum;
+#pragma unroll
+        for (int e = 0; e < E; ++e) st.o[h][e] *= alpha;
+        st.m[h] = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float vf[E];
+        Store<T>::widen(vv[u], vf);
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) st.o[h][e] = fmaf(p[u][h], vf[e], st.o[h][e]);
+        }
+    }
+}
+
 // Attend tokens [tb, te) of page-table row `pt`, taking wave-iterations
-// stream, stream + nstream, ... of TPI tokens each.
-// kbase / vbase point at this lane's 16-byte slice of slot 0's kv head.
-// Slot ids outside [0, num_slots) (malformed input) read slot 0, so no access
-// leaves the pools.
+// stream, stream + nstream, ... of TPI tokens each (one iteration's loads in
+// flight per wave).  kbase / vbase point at this lane's 16-byte slice of slot
+// 0's kv head.
 template <typename T, int D, int GQ>
 MSGL_DEV void attend_range(const int32_t *__restrict__ pt, int tb, int te, int stream, int nstream,
                            const T *__restrict__ kbase, const T *__restrict__ vbase,
                            int64_t row_elems, uint32_t num_slots, const QSlice<T> (&q)[GQ],
                            float scale_log2, int rg, SoftmaxState<T, D, GQ> &st) {
     using Geo = Geometry<T, D>;
-    constexpr int E = Geo::kEpl;
-    constexpr int LPR = Geo::kLpr;
     constexpr int RPW = Geo::kRpw;
     constexpr int U = Geo::kU;
     constexpr int TPI = Geo::kTpi;
     const int step = nstream * TPI;
     int base = tb + stream * TPI;
     if (base >= te) return;
-
     int slot[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int tok = base + u * RPW + rg;
-        slot[u] = tok < te ? pt[tok] : -1;
-    }
-    auto fetch_slot = [&](int s) -> int64_t { return (uint32_t)s < num_slots ? s : 0; };
+    load_slots<U, RPW>(slot, pt, base, te, rg);
     for (;;) {
         uint4 kv[U], vv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (slot[u] >= 0) {
-                const int64_t off = fetch_slot(slot[u]) * row_elems;
-                kv[u] = ld16_nt(kbase + off);
-                vv[u] = ld16_nt(vbase + off);
-            } else {
-                kv[u] = make_uint4(0, 0, 0, 0);
-                vv[u] = make_uint4(0, 0, 0, 0);
-            }
-        }
-        // page-table entries of this wave's next iteration, ahead of use
+        issue_kv<T, U>(kv, vv, slot, kbase, vbase, row_elems, num_slots);
         const int nbase = base + step;
         int nslot[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int tok = nbase + u * RPW + rg;
-            nslot[u] = tok < te ? pt[tok] : -1;
-        }
-        // scores (log2 units)
-        float s[U][GQ];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) {
-                const float d = group_sum<LPR>(q[h].dot(kv[u]));
-                s[u][h] = slot[u] >= 0 ? d * scale_log2 : -INFINITY;
-            }
-        }
-        // online softmax: rescale once per iteration
-        float p[U][GQ];
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-            float mx = s[0][h];
-#pragma unroll
-            for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][h]);
-            const float mn = fmaxf(st.m[h], mx);
-            const float mu = (mn == -INFINITY) ? 0.0f : mn;
-            const float alpha = fast_exp2(st.m[h] - mu);
-            float psum = 0.0f;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                p[u][h] = fast_exp2(s[u][h] - mu);
-                psum += p[u][h];
-            }
-            st.l[h] = st.l[h] * alpha + psum;
-#pragma unroll
-            for (int e = 0; e < E; ++e) st.o[h][e] *= alpha;
-            st.m[h] = mn;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float vf[E];
-            Store<T>::widen(vv[u], vf);
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) st.o[h][e] = fmaf(p[u][h], vf[e], st.o[h][e]);
-            }
-        }
+        load_slots<U, RPW>(nslot, pt, nbase, te, rg);  // ahead of use
+        consume_iter<T, D, GQ, U>(kv, vv, slot, q, scale_log2, st);
         if (nbase >= te) break;
         base = nbase;
 #pragma unroll
         for (int u = 0; u < U; ++u) slot[u] = nslot[u];
+    }
+}
+
+// Attend tokens [tb, te) with a software pipeline: page-table ids two
+// iterations ahead and K/V data one iteration ahead of the compute, so every
+// wave keeps loads in flight while it works on the previous tokens.
+template <typename T, int D, int GQ, int U>
+MSGL_DEV void attend_pipelined(const int32_t *__restrict__ pt, int tb, int te,
+                               const T *__restrict__ kbase, const T *__restrict__ vbase,
+                               int64_t row_elems, uint32_t num_slots, const QSlice<T> (&q)[GQ],
+                               float scale_log2, int rg, SoftmaxState<T, D, GQ> &st) {
+    constexpr int RPW = Geometry<T, D>::kRpw;
+    constexpr int TPI = RPW * U;
+    if (tb >= te) return;
+    int s0[U], s1[U], s2[U];
+    load_slots<U, RPW>(s0, pt, tb, te, rg);
+    load_slots<U, RPW>(s1, pt, tb + TPI, te, rg);
+    uint4 k0[U], v0[U], k1[U], v1[U];
+    issue_kv<T, U>(k0, v0, s0, kbase, vbase, row_elems, num_slots);
+    for (int base = tb; base < te; base += TPI) {
+        load_slots<U, RPW>(s2, pt, base + 2 * TPI, te, rg);
+        issue_kv<T, U>(k1, v1, s1, kbase, vbase, row_elems, num_slots);
+        consume_iter<T, D, GQ, U>(k0, v0, s0, q, scale_log2, st);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            k0[u] = k1[u];
+            v0[u] = v1[u];
+            s0[u] = s1[u];
+            s1[u] = s2[u];
+        }
     }
 }
 

@@ -5,175 +5,182 @@
 // and V slices are read once per kv head, and everything else (q, out,
 // partials, page-table ids) is small beside them.
 //
-// Work decomposition.  A request's keys are cut into chunks of `chunk`
-// tokens; a work item is (request, chunk, group of HPW kv heads).  The grid
-// is persistent (about as many 256-thread blocks as fit on the chip at once)
-// and blocks pull items from a device-side counter, so the grid does not
-// depend on the lengths: a graph captured once stays valid for any batch
-// whose lengths stay within max_seq_len, and the long tail of a lognormal
-// length mix is balanced dynamically.  Each block derives the item list from
-// seq_lens itself (a prefix sum of chunks per request in LDS).  The last
-// block to finish resets the counters, so they are zero between calls
-// without a memset.
-//
-// Inside an item, the 4 waves of the block split as HPW kv heads x (4 / HPW)
-// token streams; see attend_valu.h for the lane layout.  A request whose keys
-// fit in one chunk writes its normalised output directly; longer ones write
-// per-chunk partial states (m, l, unnormalised o) that decode_merge_kernel
-// combines with the usual log-sum-exp rescaling.
+// Work decomposition (balanced split).  Concatenate every request's keys into
+// one sequence of sum(seq_lens) tokens (per group of kv heads when there are
+// more kv heads than waves in a block) and give each block of the persistent
+// grid an equal, contiguous share of it.  A block has one wave per kv head;
+// each wave streams its share of tokens for its head with a software pipeline
+// (attend_valu.h) and no barriers.  Where a block's share covers a request
+// whole, the wave writes the normalised output; where a request straddles
+// block boundaries, each piece writes its partial softmax state (m, l,
+// unnormalised o) and decode_merge_kernel combines the pieces with the usual
+// log-sum-exp rescaling.  Equal shares balance any length mix (a lognormal tail
+// included) without a work queue, the grid does not depend on the lengths
+// (so a graph captured once serves any batch within max_seq_len), and the
+// workspace carries no state between calls.  Each block derives the prefix of
+// lengths from seq_lens itself; block 0 also leaves it (and the share) in the
+// workspace for the merge.
 #include "attend_valu.h"
 #include "launch.h"
 
 namespace msgl {
 
-template <typename T, int D, int GQ, int HPW>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+// Workspace layout (offsets in bytes):
+//   [0, 256)            control: int64 total tokens, int64 share per block
+//   [256, 256 + P)      int32 prefix of lengths [batch + 1], P rounded up to 256
+//   then                float part_o [batch + kMaxDecodeGrid][q_heads][head_dim]
+//   then                float part_ml[batch + kMaxDecodeGrid][q_heads][2]
+// A piece (request b, block j) is stored at index b + j: pieces are
+// contiguous in both orders, so no two (b, j) pairs of real pieces collide.
+
+template <typename T, int D, int GQ, int U>
+__global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
     using Geo = Geometry<T, D>;
     constexpr int E = Geo::kEpl;
     constexpr int LPR = Geo::kLpr;
-    constexpr int NSTREAM = 4 / HPW;
-    extern __shared__ int s_prefix[];  // [batch + 1] chunks before each request
-    __shared__ float s_buf[4 * GQ * (D + 2)];
-    __shared__ int s_item;
+    extern __shared__ int s_tok[];  // [batch + 1] tokens before each request
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int hw = wave % HPW;
-    const int stream = wave / HPW;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wpb = blockDim.x >> 6;  // kv heads per block
     const int rg = lane / LPR;
     const int lr = lane % LPR;
-    const int nhg = a.kv_heads / HPW;
+    const int nhg = a.kv_heads / wpb;
     const int64_t row_elems = (int64_t)a.kv_heads * D;
+    // lengths beyond the table row or max_seq_len are cut there, and
+    // non-positive ones count as empty (malformed input never leaves bounds)
+    const int lmax = (int)min(a.row_stride, (int64_t)a.max_seq_len);
 
-    // chunk counts -> exclusive prefix in LDS (wave 0, 64 requests at a time)
     if (wave == 0) {
         int carry = 0;
-        if (lane == 0) s_prefix[0] = 0;
+        if (lane == 0) s_tok[0] = 0;
         for (int base = 0; base < a.batch; base += 64) {
             const int b = base + lane;
-            int n = 0;
-            if (b < a.batch) {
-                const int L = a.seq_lens[b];
-                n = L > 0 ? min((L + a.chunk - 1) / a.chunk, a.max_splits) : 0;
-            }
+            int n = b < a.batch ? max(0, min(a.seq_lens[b], lmax)) : 0;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const int y = __shfl_up(n, off);
                 if (lane >= off) n += y;
             }
-            if (b < a.batch) s_prefix[b + 1] = carry + n;
+            if (b < a.batch) s_tok[b + 1] = carry + n;
             carry += __shfl(n, 63);
         }
     }
     __syncthreads();
-    const int total_items = s_prefix[a.batch] * nhg;
-
-    for (;;) {
-        if (tid == 0) s_item = (int)atomicAdd(&a.ctrl[0], 1u);
-        __syncthreads();
-        const int item = s_item;
-        __syncthreads();
-        if (item >= total_items) break;
-
-        const int hg = item % nhg;
-        const int pair = item / nhg;
-        int lo = 0, hi = a.batch;  // s_prefix[lo] <= pair < s_prefix[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_prefix[mid] <= pair) lo = mid; else hi = mid;
+    const int64_t total = s_tok[a.batch];
+    const int64_t work = total * nhg;
+    int64_t share = (work + gridDim.x - 1) / gridDim.x;
+    if (share < a.chunk) share = a.chunk;
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i <= a.batch; i += blockDim.x) a.prefix[i] = s_tok[i];
+        if (threadIdx.x == 0) {
+            a.ctrl[0] = total;
+            a.ctrl[1] = share;
         }
-        const int b = lo;
-        const int split = pair - s_prefix[b];
-        const int nsplit = s_prefix[b + 1] - s_prefix[b];
-        // lengths beyond the table row or the workspace's split count are cut
-        // there (malformed input must not read or write out of bounds)
-        const int L = min(a.seq_lens[b], (int)min(a.row_stride, (int64_t)a.max_splits * a.chunk));
-        const int t0 = split * a.chunk;
-        const int t1 = min(L, t0 + a.chunk);
-        const int kvh = hg * HPW + hw;
-        const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
+    }
+    int64_t cur = (int64_t)blockIdx.x * share;
+    const int64_t end = min(cur + share, work);
+    if (cur >= end) return;
 
-        QSlice<T> q[GQ];
-        const T *qp = reinterpret_cast<const T *>(a.q) +
-                      ((int64_t)b * a.q_heads + (int64_t)kvh * GQ) * D + lr * E;
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) q[h].load(qp + h * D);
+    int hg = (int)(cur / total);
+    const int64_t off = cur - (int64_t)hg * total;
+    int lo = 0, hi = a.batch;  // last b with s_tok[b] <= off
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_tok[mid] <= off) lo = mid; else hi = mid;
+    }
+    int b = lo;
+    int j = (int)(off - s_tok[b]);
 
-        SoftmaxState<T, D, GQ> st;
-        st.init();
-        const T *kb = reinterpret_cast<const T *>(a.k_pool) + (int64_t)kvh * D + lr * E;
-        const T *vb = reinterpret_cast<const T *>(a.v_pool) + (int64_t)kvh * D + lr * E;
-        attend_range<T, D, GQ>(pt, t0, t1, stream, NSTREAM, kb, vb, row_elems, (uint32_t)a.num_slots, q,
-                               a.scale_log2, rg, st);
-        st.template reduce_wave<LPR>();
-        merge_streams<T, D, GQ>(st, s_buf, wave, stream, NSTREAM, lane, lr, rg);
-
-        if (stream == 0 && rg == 0) {
-            const int qh0 = kvh * GQ;
-            if (nsplit == 1) {
+    while (cur < end) {
+        const int L = s_tok[b + 1] - s_tok[b];
+        const int je = (int)min((int64_t)L, (int64_t)j + (end - cur));
+        if (je > j) {
+            const int kvh = hg * wpb + wave;
+            const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
+            QSlice<T> q[GQ];
+            const T *qp = reinterpret_cast<const T *>(a.q) +
+                          ((int64_t)b * a.q_heads + (int64_t)kvh * GQ) * D + lr * E;
 #pragma unroll
-                for (int h = 0; h < GQ; ++h) {
-                    const float inv = 1.0f / st.l[h];
-                    float f[E];
+            for (int h = 0; h < GQ; ++h) q[h].load(qp + h * D);
+            SoftmaxState<T, D, GQ> st;
+            st.init();
+            const T *kb = reinterpret_cast<const T *>(a.k_pool) + (int64_t)kvh * D + lr * E;
+            const T *vb = reinterpret_cast<const T *>(a.v_pool) + (int64_t)kvh * D + lr * E;
+            attend_pipelined<T, D, GQ, U>(pt, j, je, kb, vb, row_elems, (uint32_t)a.num_slots, q,
+                                          a.scale_log2, rg, st);
+            st.template reduce_wave<LPR>();
+            if (rg == 0) {
+                const int qh0 = kvh * GQ;
+                if (j == 0 && je == L) {
 #pragma unroll
-                    for (int e = 0; e < E; ++e) f[e] = st.o[h][e] * inv;
-                    T *op = reinterpret_cast<T *>(a.out) + ((int64_t)b * a.q_heads + qh0 + h) * D +
-                            lr * E;
-                    st16(op, Store<T>::narrow(f));
-                    if (a.lse != nullptr && lr == 0)
-                        a.lse[(int64_t)b * a.q_heads + qh0 + h] = (st.m[h] + __log2f(st.l[h])) * kLn2;
-                }
-            } else {
-                const int64_t base = ((int64_t)b * a.max_splits + split) * a.q_heads + qh0;
+                    for (int h = 0; h < GQ; ++h) {
+                        const float inv = 1.0f / st.l[h];
+                        float f[E];
 #pragma unroll
-                for (int h = 0; h < GQ; ++h) {
-                    float *po = a.part_o + (base + h) * D + lr * E;
+                        for (int e = 0; e < E; ++e) f[e] = st.o[h][e] * inv;
+                        T *op = reinterpret_cast<T *>(a.out) + ((int64_t)b * a.q_heads + qh0 + h) * D +
+                                lr * E;
+                        st16(op, Store<T>::narrow(f));
+                        if (a.lse != nullptr && lr == 0)
+                            a.lse[(int64_t)b * a.q_heads + qh0 + h] = (st.m[h] + __log2f(st.l[h])) * kLn2;
+                    }
+                } else {
+                    const int64_t base = ((int64_t)b + blockIdx.x) * a.q_heads + qh0;
 #pragma unroll
-                    for (int e = 0; e < E; e += 4)
-                        *reinterpret_cast<float4 *>(po + e) =
-                            make_float4(st.o[h][e], st.o[h][e + 1], st.o[h][e + 2], st.o[h][e + 3]);
-                    if (lr == 0) {
-                        a.part_ml[(base + h) * 2] = st.m[h];
-                        a.part_ml[(base + h) * 2 + 1] = st.l[h];
+                    for (int h = 0; h < GQ; ++h) {
+                        float *po = a.part_o + (base + h) * D + lr * E;
+#pragma unroll
+                        for (int e = 0; e < E; e += 4)
+                            *reinterpret_cast<float4 *>(po + e) =
+                                make_float4(st.o[h][e], st.o[h][e + 1], st.o[h][e + 2], st.o[h][e + 3]);
+                        if (lr == 0) {
+                            a.part_ml[(base + h) * 2] = st.m[h];
+                            a.part_ml[(base + h) * 2 + 1] = st.l[h];
+                        }
                     }
                 }
             }
         }
-    }
-
-    // every block has taken its last item: the last one out resets the counters
-    if (tid == 0) {
-        const unsigned done = atomicAdd(&a.ctrl[1], 1u);
-        if (done == gridDim.x - 1) {
-            atomicExch(&a.ctrl[0], 0u);
-            atomicExch(&a.ctrl[1], 0u);
+        cur += je - j;
+        j = je;
+        if (j >= L) {
+            j = 0;
+            if (++b == a.batch) {
+                b = 0;
+                ++hg;
+            }
         }
     }
 }
 
-// Combine the chunk partials of every request with more than one chunk.
+// Combine the pieces of every request that straddles block boundaries.
 // One wave per (request, q head); each lane owns D / 64 output elements.
-template <typename T, int D>
+template <typename T, int D, int GQ>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     constexpr int PER = D / 64;
     const int b = blockIdx.x;
     const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (h >= a.q_heads) return;
-    const int L = a.seq_lens[b];
-    const int nsplit = L > 0 ? min((L + a.chunk - 1) / a.chunk, a.max_splits) : 0;
-    if (nsplit <= 1) return;
-    const int64_t base = (int64_t)b * a.max_splits * a.q_heads + h;
-    const int64_t sstride = a.q_heads;
+    const int64_t total = a.ctrl[0];
+    const int64_t share = a.ctrl[1];
+    const int L = a.prefix[b + 1] - a.prefix[b];
+    if (L <= 0) return;
+    const int hg = (h / GQ) / a.wpb;
+    const int64_t first_tok = (int64_t)hg * total + a.prefix[b];
+    const int first = (int)(first_tok / share);
+    const int last = (int)((first_tok + L - 1) / share);
+    if (first == last) return;  // one piece: the split kernel wrote the output
     float mx = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, a.part_ml[(base + s * sstride) * 2]);
+    for (int j = first; j <= last; ++j) mx = fmaxf(mx, a.part_ml[(((int64_t)b + j) * a.q_heads + h) * 2]);
     float l = 0.0f;
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-        const int64_t idx = base + s * sstride;
+#pragma unroll 4
+    for (int j = first; j <= last; ++j) {
+        const int64_t idx = ((int64_t)b + j) * a.q_heads + h;
         const float w = fast_exp2(a.part_ml[idx * 2] - mx);
         l = fmaf(a.part_ml[idx * 2 + 1], w, l);
         const float *po = a.part_o + idx * D + lane * PER;
@@ -213,52 +220,79 @@ int device_cu_count() {
     return cached[dev];
 }
 
-template <typename T, int D, int GQ, int HPW>
-int decode_occupancy(int batch) {
-    static int occ = 0;  // blocks per CU at this instantiation's resource use
-    if (occ == 0) {
+// Loads per wave-iteration of the decode pipeline (4 tokens per load for
+// 256-byte head slices: 16 tokens per iteration).
+template <typename T, int D>
+constexpr int decode_unroll() {
+#ifdef MSGL_DECODE_UNROLL  // tuning builds only
+    return MSGL_DECODE_UNROLL;
+#else
+    return Geometry<T, D>::kU;
+#endif
+}
+
+template <typename T, int D, int GQ>
+int decode_occupancy(int threads, int batch) {
+    static int occ[17] = {0};  // blocks per CU, by waves per block
+    const int w = threads / 64;
+    if (occ[w] == 0) {
         const size_t smem = sizeof(int) * (size_t)(batch + 1);
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<T, D, GQ, HPW>, 256,
-                                                         smem + 4096) != hipSuccess || n <= 0)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &n, decode_split_kernel<T, D, GQ, decode_unroll<T, D>()>, threads, smem + 4096) != hipSuccess ||
+            n <= 0)
             n = 1;
-        occ = n;
+        occ[w] = n;
     }
-    return occ;
+    return occ[w];
 }
 
 // prepare_only: resolve the cached device queries (CU count, occupancy) and
 // launch nothing; used before stream capture.
-template <typename T, int D, int GQ, int HPW>
-hipError_t run_decode(const DecodeArgs &a, hipStream_t stream, bool prepare_only) {
-    const int occ = decode_occupancy<T, D, GQ, HPW>(a.batch);
+// Waves (kv heads) per decode block: the largest power of two up to
+// kDecodeWaves that divides kv_heads.
+int decode_waves(int kv_heads) {
+#ifdef MSGL_DECODE_WPB  // tuning builds only
+    constexpr int kDecodeWaves = MSGL_DECODE_WPB;
+#else
+    constexpr int kDecodeWaves = 4;
+#endif
+    int w = kDecodeWaves;
+    while (w > 1 && kv_heads % w != 0) w >>= 1;
+    return w;
+}
+
+template <typename T, int D, int GQ>
+hipError_t run_decode(const DecodeArgs &a_in, hipStream_t stream, bool prepare_only) {
+    DecodeArgs a = a_in;
+    a.wpb = decode_waves(a.kv_heads);
+    const int threads = 64 * a.wpb;
+#ifdef MSGL_DECODE_BLOCKS_PER_CU  // tuning builds only
+    const int occ = MSGL_DECODE_BLOCKS_PER_CU;
+#else
+    const int occ = decode_occupancy<T, D, GQ>(threads, a.batch);
+#endif
     const int cus = device_cu_count();
     if (prepare_only) return hipSuccess;
-    const size_t smem = sizeof(int) * (size_t)(a.batch + 1);
-    const int64_t max_items = (int64_t)a.batch * a.max_splits * (a.kv_heads / HPW);
     int64_t grid = (int64_t)cus * occ;
-    if (grid > max_items) grid = max_items;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, GQ, HPW>), dim3((unsigned)grid), dim3(256), smem, stream, a);
+    if (grid > kMaxDecodeGrid) grid = kMaxDecodeGrid;
+    const size_t smem = sizeof(int) * (size_t)(a.batch + 1);
+    hipLaunchKernelGGL((decode_split_kernel<T, D, GQ, decode_unroll<T, D>()>), dim3((unsigned)grid),
+                       dim3(threads), smem, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.max_splits > 1) {
-        hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.batch, (a.q_heads + 3) / 4), dim3(256), 0,
-                           stream, a);
-        e = hipGetLastError();
-    }
-    return e;
+    hipLaunchKernelGGL((decode_merge_kernel<T, D, GQ>), dim3(a.batch, (a.q_heads + 3) / 4), dim3(256), 0, stream,
+                       a);
+    return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t run_decode_g(const DecodeArgs &a, hipStream_t stream, bool prep) {
-    const int g = a.q_heads / a.kv_heads;
-    const bool two = (a.kv_heads % 2) == 0;
-    switch (g) {
-        case 1: return two ? run_decode<T, D, 1, 2>(a, stream, prep) : run_decode<T, D, 1, 1>(a, stream, prep);
-        case 2: return two ? run_decode<T, D, 2, 2>(a, stream, prep) : run_decode<T, D, 2, 1>(a, stream, prep);
-        case 4: return two ? run_decode<T, D, 4, 2>(a, stream, prep) : run_decode<T, D, 4, 1>(a, stream, prep);
-        case 8: return two ? run_decode<T, D, 8, 2>(a, stream, prep) : run_decode<T, D, 8, 1>(a, stream, prep);
+    switch (a.q_heads / a.kv_heads) {
+        case 1: return run_decode<T, D, 1>(a, stream, prep);
+        case 2: return run_decode<T, D, 2>(a, stream, prep);
+        case 4: return run_decode<T, D, 4>(a, stream, prep);
+        case 8: return run_decode<T, D, 8>(a, stream, prep);
         default: return hipErrorInvalidValue;
     }
 }
@@ -266,10 +300,10 @@ hipError_t run_decode_g(const DecodeArgs &a, hipStream_t stream, bool prep) {
 }  // namespace
 
 size_t decode_workspace_bytes(int batch, int q_heads, int head_dim, int max_seq_len, int chunk) {
-    if (chunk <= 0) chunk = kDefaultChunk;
-    const size_t max_splits = ((size_t)max_seq_len + chunk - 1) / chunk;
-    const size_t parts = (size_t)batch * max_splits * q_heads;
-    return kCtrlBytes + parts * head_dim * sizeof(float) + parts * 2 * sizeof(float);
+    (void)max_seq_len;
+    (void)chunk;
+    const size_t pieces = (size_t)batch + kMaxDecodeGrid;
+    return kCtrlBytes + decode_prefix_bytes(batch) + pieces * q_heads * ((size_t)head_dim + 2) * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, DType dtype, int head_dim, hipStream_t stream,

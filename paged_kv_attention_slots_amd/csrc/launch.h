@@ -11,10 +11,14 @@ enum DType { kF32 = 0, kBF16 = 1 };
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
-// Decode split size used when the caller passes chunk == 0.
-constexpr int kDefaultChunk = 256;
-// Bytes of the decode workspace's control block (work-queue counters).
+// Minimum keys per decode block (the `chunk` argument) when the caller passes 0.
+constexpr int kDefaultChunk = 128;
+// Bytes of the decode workspace's control block.
 constexpr size_t kCtrlBytes = 256;
+// Upper bound of the decode grid (it sizes the workspace's partial states).
+constexpr int kMaxDecodeGrid = 4096;
+
+inline size_t decode_prefix_bytes(int batch) { return ((size_t)(batch + 1) * 4 + 255) / 256 * 256; }
 
 struct StoreKvArgs {
     void *k_pool;
@@ -41,12 +45,14 @@ struct DecodeArgs {
     int32_t batch;
     int32_t q_heads;
     int32_t kv_heads;
-    int32_t chunk;
-    int32_t max_splits;
-    float scale_log2;  // sm_scale * log2(e)
-    float *part_o;     // [batch, max_splits, q_heads, head_dim]
-    float *part_ml;    // [batch, max_splits, q_heads, 2]  (max in log2 units, sum)
-    uint32_t *ctrl;    // [2] work-queue counter, finished-group counter (zero between calls)
+    int32_t chunk;        // minimum keys per block
+    int32_t wpb;          // waves (kv heads) per decode block
+    int32_t max_seq_len;  // lengths are cut at min(max_seq_len, row_stride)
+    float scale_log2;     // sm_scale * log2(e)
+    int64_t *ctrl;        // [2] total keys, keys per block (written by the split kernel)
+    int32_t *prefix;      // [batch + 1] keys before each request (written by the split kernel)
+    float *part_o;        // [batch + kMaxDecodeGrid, q_heads, head_dim]
+    float *part_ml;       // [batch + kMaxDecodeGrid, q_heads, 2]  (max in log2 units, sum)
 };
 
 struct PrefillArgs {

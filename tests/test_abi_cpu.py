@@ -87,10 +87,11 @@ def test_decode_argument_checks(L):
 
 
 def test_decode_workspace_size_formula(L):
-    # control block + (m, l, o[d]) float32 per (request, chunk, q head)
-    bs, H, d, msl, chunk = 256, 32, 128, 32768, 256
-    splits = (msl + chunk - 1) // chunk
-    assert L.msgl_decode_workspace_bytes(bs, H, d, msl, chunk) == 256 + bs * splits * H * (d + 2) * 4
+    # control block + length prefix + (m, l, o[d]) float32 per (piece, q head),
+    # with at most batch + 4096 pieces
+    bs, H, d, msl = 256, 32, 128, 32768
+    prefix = ((bs + 1) * 4 + 255) // 256 * 256
+    assert L.msgl_decode_workspace_bytes(bs, H, d, msl, 256) == 256 + prefix + (bs + 4096) * H * (d + 2) * 4
     assert L.msgl_decode_workspace_bytes(bs, H, d, msl, 0) == L.msgl_decode_workspace_bytes(bs, H, d, msl, 256)
 
 
