@@ -1,9 +1,287 @@
-// Prefill / extend attention on matrix cores (bf16 MFMA) - dispatch.
+// Prefill / extend attention on matrix cores (bf16 MFMA, fp32 accumulate).
+//
+// New token i of request b sits at position p = cached_len + i and attends
+// keys 0..p of its page-table row: a causal mask offset by the cached prefix.
+//
+// Block = one kv head x one block of query tokens.  Its 128 "columns" are
+// (token, q head) pairs of the q heads that share the kv head (token-major),
+// so every gathered K/V tile serves all of them.  Each of the 4 waves owns 32
+// columns.  Keys stream through LDS in tiles of 64, double-buffered: the next
+// tile's gathers (slot ids from the page table, then 256-byte K and V rows)
+// are in flight while the current tile computes.  K is stored row-major; V is
+// stored transposed (dims x keys) so that it can feed the A operand below.
+//
+// Per 32 keys a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+// (A = 32 keys x 16 dims from LDS, B = Q^T held in registers, 8 steps over
+// head_dim 128).  The MFMA result layout leaves each lane with 16 scores of
+// one column; after the softmax update they are rounded to bf16 and are,
+// unchanged, the B operand (P^T) of O^T += V^T P^T, because the order of the
+// contraction index inside an MFMA is free as long as both operands agree:
+// the V^T reads pick the keys in the order the scores arrived in.  Nothing is
+// shuffled between lanes except one exchange for the column max.
+//
+// Softmax: log2 domain (scale folded with log2 e), running max per column,
+// lane-partial running sums (reduced once at the end), and lazy rescaling:
+// the output is only rescaled when a column's max grows by more than 2^8,
+// which keeps exp2 arguments bounded and skips almost every rescale.  The
+// output is normalised by the sum of the bf16-rounded probabilities that the
+// P.V product uses, so the applied weights sum to one; the returned lse comes
+// from the sum of the unrounded ones.
+//
+// Blocks are ordered longest-first (last query blocks, which see the most
+// keys, get the lowest block ids) so the ragged tail balances.
+#include "common.h"
 #include "launch.h"
 
 namespace msgl {
 
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
+
+namespace pf {
+constexpr int kD = 128;
+constexpr int kKT = 64;                        // keys per LDS tile
+constexpr int kWaves = 4;
+constexpr int kColsW = 32;                     // query columns per wave
+constexpr int kCols = kWaves * kColsW;         // query columns per block
+constexpr int kKStride = kD * 2 + 16;          // bytes per key row of the K tile (padded)
+constexpr int kVStride = (kKT + 4) * 2;        // bytes per dim row of the V^T tile (padded)
+constexpr int kKBytes = kKT * kKStride;
+constexpr int kVBytes = kD * kVStride;
+constexpr int kStage = kKBytes + kVBytes;
+constexpr float kRescaleLog2 = 8.0f;
+}  // namespace pf
+
+MSGL_DEV floatx16_t mfma_32x32x16(const bf16x8_t &a, const bf16x8_t &b, const floatx16_t &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+MSGL_DEV uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+
+// A tile's gathers for one thread: keys 4*grp .. 4*grp+3, dims 8*sl .. 8*sl+7.
+struct TileRegs {
+    uint4 k[4];
+    uint4 v[4];
+};
+
+MSGL_DEV void tile_load(TileRegs &r, const int32_t *__restrict__ pt, int k0, int nkeys,
+                        const bf16_t *__restrict__ kh, const bf16_t *__restrict__ vh, int64_t row_elems,
+                        uint32_t num_slots, int tid) {
+    const int grp = tid >> 4;
+    const int sl = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int key = k0 + 4 * grp + i;
+        if (key < nkeys) {
+            int slot = pt[key];
+            if ((uint32_t)slot >= num_slots) slot = 0;  // malformed id: stay inside the pool
+            const int64_t off = (int64_t)slot * row_elems + sl * 8;
+            r.k[i] = ld16(kh + off);
+            r.v[i] = ld16(vh + off);
+        } else {
+            r.k[i] = make_uint4(0, 0, 0, 0);  // keys past the end: zero rows (masked anyway)
+            r.v[i] = make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+MSGL_DEV uint32_t comp(const uint4 &v, int p) { return p == 0 ? v.x : p == 1 ? v.y : p == 2 ? v.z : v.w; }
+
+MSGL_DEV void tile_store(const TileRegs &r, char *stage, int tid) {
+    const int grp = tid >> 4;
+    const int sl = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4 *>(stage + (4 * grp + i) * pf::kKStride + sl * 16) = r.k[i];
+    char *vt = stage + pf::kKBytes;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t w0 = comp(r.v[0], p), w1 = comp(r.v[1], p), w2 = comp(r.v[2], p), w3 = comp(r.v[3], p);
+        // dim 8*sl + 2p: the low halves of the 4 keys; dim 8*sl + 2p + 1: the high halves
+        const uint2 lo = make_uint2(perm_b32(w1, w0, 0x05040100u), perm_b32(w3, w2, 0x05040100u));
+        const uint2 hi = make_uint2(perm_b32(w1, w0, 0x07060302u), perm_b32(w3, w2, 0x07060302u));
+        *reinterpret_cast<uint2 *>(vt + (sl * 8 + 2 * p) * pf::kVStride + grp * 8) = lo;
+        *reinterpret_cast<uint2 *>(vt + (sl * 8 + 2 * p + 1) * pf::kVStride + grp * 8) = hi;
+    }
+}
+
+template <int GQ>
+__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int nqb) {
+    constexpr int BQ = pf::kCols / GQ;  // query tokens per block
+    __shared__ __attribute__((aligned(16))) char smem[2 * pf::kStage];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int jj = lane >> 5;
+    const int G = a.kv_heads;
+
+    int idx = blockIdx.x;  // longest first: query block index descends with the block id
+    const int kvh = idx % G;
+    idx /= G;
+    const int b = idx % a.batch;
+    idx /= a.batch;
+    const int qb = nqb - 1 - idx;
+    const int L = (int)min((int64_t)a.seq_lens[b], a.row_stride);
+    const int C = a.cached_lens[b];
+    const int E = L - C;
+    const int t0 = qb * BQ;
+    if (qb < 0 || C < 0 || t0 >= E) return;  // uniform over the block, before any barrier
+    const int row0 = a.cu_q[b] + t0;
+    const int ntok = min(min(BQ, E - t0), a.total_q - row0);
+    if (ntok <= 0) return;
+    const int pos0 = C + t0;         // position of the block's first token
+    const int nkeys = pos0 + ntok;   // keys 0 .. position of its last token
+
+    // this lane's query column
+    const int col = wave * pf::kColsW + (lane & 31);
+    const int tl = col / GQ;
+    const int hq = kvh * GQ + col % GQ;
+    const bool valid = tl < ntok;
+    const int tok = valid ? tl : ntok - 1;
+    const int pos = pos0 + tok;
+
+    // Q^T operands: d-chunk dc holds dims 16*dc + 8*jj .. +7 of this column
+    bf16x8_t qv[8];
+    const bf16_t *qp = reinterpret_cast<const bf16_t *>(a.q) +
+                       ((int64_t)(row0 + tok) * a.q_heads + hq) * pf::kD + 8 * jj;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) qv[dc] = __builtin_bit_cast(bf16x8_t, ld16(qp + 16 * dc));
+
+    floatx16_t acc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = floatx16_t{};
+    float m = -INFINITY;  // running column max (log2 units; may lag by < 2^8)
+    float l = 0.0f;       // this lane's share of the running sum of the bf16-rounded weights
+    float lt = 0.0f;      // the same for the unrounded weights (for lse)
+
+    const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
+    const bf16_t *kh = reinterpret_cast<const bf16_t *>(a.k_pool) + (int64_t)kvh * pf::kD;
+    const bf16_t *vh = reinterpret_cast<const bf16_t *>(a.v_pool) + (int64_t)kvh * pf::kD;
+    const int64_t row_elems = (int64_t)G * pf::kD;
+    const uint32_t num_slots = (uint32_t)a.num_slots;
+    const int ntiles = (nkeys + pf::kKT - 1) / pf::kKT;
+
+    TileRegs r;
+    tile_load(r, pt, 0, nkeys, kh, vh, row_elems, num_slots, tid);
+    tile_store(r, smem, tid);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const char *st = smem + (t & 1) * pf::kStage;
+        const bool more = t + 1 < ntiles;
+        if (more) tile_load(r, pt, (t + 1) * pf::kKT, nkeys, kh, vh, row_elems, num_slots, tid);
+        const int k0 = t * pf::kKT;
+        const bool need_mask = k0 + pf::kKT - 1 > pos0;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int kb = half * 32;
+            floatx16_t s = floatx16_t{};
+            const char *krow = st + (kb + (lane & 31)) * pf::kKStride + 16 * jj;
+#pragma unroll
+            for (int dc = 0; dc < 8; ++dc)
+                s = mfma_32x32x16(*reinterpret_cast<const bf16x8_t *>(krow + 32 * dc), qv[dc], s);
+
+            float sv[16];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float v = s[e] * a.scale_log2;
+                if (need_mask) {
+                    const int key = k0 + kb + 8 * (e >> 2) + 4 * jj + (e & 3);
+                    v = key > pos ? -INFINITY : v;
+                }
+                sv[e] = v;
+                mx = fmaxf(mx, v);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (__any(mx > m + pf::kRescaleLog2)) {
+                const float mn = fmaxf(m, mx);
+                const float alpha = (mn == -INFINITY) ? 1.0f : fast_exp2(m - mn);
+                l *= alpha;
+                lt *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+                m = mn;
+            }
+            const float mu = (m == -INFINITY) ? 0.0f : m;
+            uint32_t pw[8];
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const float p0 = fast_exp2(sv[e] - mu);
+                const float p1 = fast_exp2(sv[e + 1] - mu);
+                const uint32_t w = pack_bf16x2(p0, p1);
+                pw[e >> 1] = w;
+                l += bf16_lo(w) + bf16_hi(w);
+                lt += p0 + p1;
+            }
+            const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+            const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+
+            const char *vt = st + pf::kKBytes + (lane & 31) * pf::kVStride + (kb + 4 * jj) * 2;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const char *vrow = vt + db * 32 * pf::kVStride;
+                const uint2 a0 = *reinterpret_cast<const uint2 *>(vrow);
+                const uint2 a1 = *reinterpret_cast<const uint2 *>(vrow + 16);
+                const uint2 a2 = *reinterpret_cast<const uint2 *>(vrow + 32);
+                const uint2 a3 = *reinterpret_cast<const uint2 *>(vrow + 48);
+                acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y)), pb0,
+                                        acc[db]);
+                acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(a2.x, a2.y, a3.x, a3.y)), pb1,
+                                        acc[db]);
+            }
+        }
+        if (more) tile_store(r, smem + ((t + 1) & 1) * pf::kStage, tid);
+        __syncthreads();
+    }
+
+    l += __shfl_xor(l, 32);
+    lt += __shfl_xor(lt, 32);
+    if (valid) {
+        const float inv = 1.0f / l;
+        bf16_t *op = reinterpret_cast<bf16_t *>(a.out) + ((int64_t)(row0 + tl) * a.q_heads + hq) * pf::kD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = db * 32 + 8 * i + 4 * jj;
+                *reinterpret_cast<uint2 *>(op + d0) =
+                    make_uint2(pack_bf16x2(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv),
+                               pack_bf16x2(acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv));
+            }
+        if (a.lse != nullptr && jj == 0) a.lse[(int64_t)(row0 + tl) * a.q_heads + hq] = (m + __log2f(lt)) * kLn2;
+    }
+}
+
+namespace {
+
+template <int GQ>
+hipError_t run_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
+    constexpr int BQ = pf::kCols / GQ;
+    const int nqb = (a.max_extend + BQ - 1) / BQ;
+    const int64_t grid = (int64_t)nqb * a.batch * a.kv_heads;
+    if (grid < 1) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_mfma_kernel<GQ>), dim3((unsigned)grid), dim3(256), 0, stream, a, nqb);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_prefill(const PrefillArgs &a, DType dtype, int head_dim, hipStream_t stream) {
+    if (dtype == kBF16 && head_dim == pf::kD) {
+        switch (a.q_heads / a.kv_heads) {
+            case 1: return run_prefill_mfma<1>(a, stream);
+            case 2: return run_prefill_mfma<2>(a, stream);
+            case 4: return run_prefill_mfma<4>(a, stream);
+            case 8: return run_prefill_mfma<8>(a, stream);
+            default: break;
+        }
+    }
     return launch_prefill_valu(a, dtype, head_dim, stream);
 }
 

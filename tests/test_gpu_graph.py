@@ -75,17 +75,19 @@ def test_graph_padded_replay_matches_eager_and_oracle(oracle_mod, mods, page_siz
         torch.cuda.synchronize()  # the copies ran on the default stream
         g.launch(stream)
         stream.synchronize()
-        step = wl.subset_decode(base, real)
-        step.seq_lens, step.cached_lens, step.out_loc = seq, seq - 1, loc
-        step.k_new, step.v_new, step.q = k_new, v_new, q
+        # eager twin: the same padded batch through the eager entry points
+        step = wl.pad_decode(wl.subset_decode(base, real), padded)
+        for k in ("q", "k_new", "v_new", "out_loc", "table_idx", "seq_lens"):
+            setattr(step, k, buf[k].clone())
+        step.cached_lens = step.seq_lens - 1
         runner.store_kv(step, kp_e, vp_e)
         out_e, lse_e = runner.decode_attn(step, kp_e, vp_e)
         torch.cuda.synchronize()
-        assert torch.equal(out[:real].view(torch.int16), out_e.view(torch.int16)), f"round {r}"
-        assert torch.equal(lse[:real], lse_e)
+        assert torch.equal(out[:real].view(torch.int16), out_e[:real].view(torch.int16)), f"round {r}"
+        assert torch.equal(lse[:real], lse_e[:real])
         # oracle on host copies of the same inputs
         kp_h, vp_h = oracle_mod.store_kv(kp_h, vp_h, k_new, v_new, loc)
-        ref, _ = oracle_mod.attention(q, kp_h, vp_h, base.page_table, step.table_idx, seq,
+        ref, _ = oracle_mod.attention(q, kp_h, vp_h, base.page_table, base.table_idx[:real], seq,
                                       torch.arange(real + 1, dtype=torch.int32))
         err = max_abs(out[:real], ref)
         say(f"[graph] round {r}: max-abs vs oracle {err:.3e}")
