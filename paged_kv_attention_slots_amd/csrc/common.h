@@ -29,8 +29,12 @@ MSGL_DEV uint32_t f32_to_bf16_bits(float f) {
     return u >> 16;
 }
 
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float floatx2_t;
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 MSGL_DEV uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    const floatx2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // fp32 += a.bf16[0]*b.bf16[0] + a.bf16[1]*b.bf16[1]

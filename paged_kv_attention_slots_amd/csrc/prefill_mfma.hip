@@ -6,9 +6,10 @@
 // Block = one kv head x one block of query tokens.  Its 128 "columns" are
 // (token, q head) pairs of the q heads that share the kv head (token-major),
 // so every gathered K/V tile serves all of them.  Each of the 4 waves owns 32
-// columns.  Keys stream through LDS in tiles of 64, double-buffered: the next
-// tile's gathers (slot ids from the page table, then 256-byte K and V rows)
-// are in flight while the current tile computes.  K is stored row-major; V is
+// columns.  Keys stream through LDS in tiles of 64, double-buffered, with the
+// gathers pipelined: page-table slot ids are read two tiles ahead and the
+// 256-byte K and V rows of the next tile are in flight while the current tile
+// computes.  K is stored row-major; V is
 // stored transposed (dims x keys) so that it can feed the A operand below.
 //
 // Per 32 keys a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
@@ -20,13 +21,14 @@
 // the V^T reads pick the keys in the order the scores arrived in.  Nothing is
 // shuffled between lanes except one exchange for the column max.
 //
-// Softmax: log2 domain (scale folded with log2 e), running max per column,
-// lane-partial running sums (reduced once at the end), and lazy rescaling:
-// the output is only rescaled when a column's max grows by more than 2^8,
-// which keeps exp2 arguments bounded and skips almost every rescale.  The
-// output is normalised by the sum of the bf16-rounded probabilities that the
-// P.V product uses, so the applied weights sum to one; the returned lse comes
-// from the sum of the unrounded ones.
+// Softmax: log2 domain (scale times log2 e folded into one fma before exp2),
+// running max per column and lazy rescaling: the output is only rescaled when
+// a column's max grows by more than 2^8, which keeps exp2 arguments bounded
+// and skips almost every rescale.  The output is normalised by the sum of the
+// bf16-rounded probabilities that the P.V product uses, so the applied weights
+// sum to one; that sum is itself two more MFMAs (an all-ones A operand times
+// P^T gives the column sums in every row).  The returned lse comes from a
+// lane-partial fp32 sum of the unrounded weights, reduced once at the end.
 //
 // Blocks are ordered longest-first (last query blocks, which see the most
 // keys, get the lowest block ids) so the ragged tail balances.
@@ -65,18 +67,24 @@ struct TileRegs {
     uint4 v[4];
 };
 
-MSGL_DEV void tile_load(TileRegs &r, const int32_t *__restrict__ pt, int k0, int nkeys,
-                        const bf16_t *__restrict__ kh, const bf16_t *__restrict__ vh, int64_t row_elems,
-                        uint32_t num_slots, int tid) {
+// Slot ids of a thread's 4 keys in the tile starting at k0 (-1 past nkeys).
+MSGL_DEV void tile_slots(int (&slot)[4], const int32_t *__restrict__ pt, int k0, int nkeys, int tid) {
     const int grp = tid >> 4;
-    const int sl = tid & 15;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int key = k0 + 4 * grp + i;
-        if (key < nkeys) {
-            int slot = pt[key];
-            if ((uint32_t)slot >= num_slots) slot = 0;  // malformed id: stay inside the pool
-            const int64_t off = (int64_t)slot * row_elems + sl * 8;
+        slot[i] = key < nkeys ? pt[key] : -1;
+    }
+}
+
+MSGL_DEV void tile_fetch(TileRegs &r, const int (&slot)[4], const bf16_t *__restrict__ kh,
+                         const bf16_t *__restrict__ vh, int64_t row_elems, uint32_t num_slots, int tid) {
+    const int sl = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (slot[i] >= 0) {
+            const int64_t s = (uint32_t)slot[i] < num_slots ? slot[i] : 0;  // malformed id: stay in the pool
+            const int64_t off = s * row_elems + sl * 8;
             r.k[i] = ld16(kh + off);
             r.v[i] = ld16(vh + off);
         } else {
@@ -153,8 +161,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = floatx16_t{};
     float m = -INFINITY;  // running column max (log2 units; may lag by < 2^8)
-    float l = 0.0f;       // this lane's share of the running sum of the bf16-rounded weights
-    float lt = 0.0f;      // the same for the unrounded weights (for lse)
+    float lt = 0.0f;      // this lane's share of the running sum of the weights (for lse)
+    floatx16_t acc_l = floatx16_t{};  // running sum of the bf16-rounded weights (any element)
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u,
+                                                                  0x3f803f80u));
 
     const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
     const bf16_t *kh = reinterpret_cast<const bf16_t *>(a.k_pool) + (int64_t)kvh * pf::kD;
@@ -163,15 +173,20 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
     const uint32_t num_slots = (uint32_t)a.num_slots;
     const int ntiles = (nkeys + pf::kKT - 1) / pf::kKT;
 
+    // pipeline: slot ids two tiles ahead, K/V rows one tile ahead, LDS double-buffered
     TileRegs r;
-    tile_load(r, pt, 0, nkeys, kh, vh, row_elems, num_slots, tid);
+    int slot0[4], slot1[4], slot2[4];
+    tile_slots(slot0, pt, 0, nkeys, tid);
+    tile_slots(slot1, pt, pf::kKT, nkeys, tid);
+    tile_fetch(r, slot0, kh, vh, row_elems, num_slots, tid);
     tile_store(r, smem, tid);
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
         const char *st = smem + (t & 1) * pf::kStage;
         const bool more = t + 1 < ntiles;
-        if (more) tile_load(r, pt, (t + 1) * pf::kKT, nkeys, kh, vh, row_elems, num_slots, tid);
+        tile_slots(slot2, pt, (t + 2) * pf::kKT, nkeys, tid);
+        if (more) tile_fetch(r, slot1, kh, vh, row_elems, num_slots, tid);
         const int k0 = t * pf::kKT;
         const bool need_mask = k0 + pf::kKT - 1 > pos0;
 #pragma unroll
@@ -183,43 +198,44 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
             for (int dc = 0; dc < 8; ++dc)
                 s = mfma_32x32x16(*reinterpret_cast<const bf16x8_t *>(krow + 32 * dc), qv[dc], s);
 
-            float sv[16];
-            float mx = -INFINITY;
+            // column max of the raw scores (the scale is positive), masked keys excluded
+            if (need_mask) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float v = s[e] * a.scale_log2;
-                if (need_mask) {
+                for (int e = 0; e < 16; ++e) {
                     const int key = k0 + kb + 8 * (e >> 2) + 4 * jj + (e & 3);
-                    v = key > pos ? -INFINITY : v;
+                    s[e] = key > pos ? -INFINITY : s[e];
                 }
-                sv[e] = v;
-                mx = fmaxf(mx, v);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            float mx = s[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
             if (__any(mx > m + pf::kRescaleLog2)) {
                 const float mn = fmaxf(m, mx);
                 const float alpha = (mn == -INFINITY) ? 1.0f : fast_exp2(m - mn);
-                l *= alpha;
                 lt *= alpha;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc_l[e] *= alpha;
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
                 m = mn;
             }
-            const float mu = (m == -INFINITY) ? 0.0f : m;
+            const float nmu = (m == -INFINITY) ? 0.0f : -m;
             uint32_t pw[8];
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-                const float p0 = fast_exp2(sv[e] - mu);
-                const float p1 = fast_exp2(sv[e + 1] - mu);
-                const uint32_t w = pack_bf16x2(p0, p1);
-                pw[e >> 1] = w;
-                l += bf16_lo(w) + bf16_hi(w);
+                const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, nmu));
+                const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, nmu));
+                pw[e >> 1] = pack_bf16x2(p0, p1);
                 lt += p0 + p1;
             }
             const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
             const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+            // running sum of the rounded weights: every row of ones . P^T is the column sum
+            acc_l = mfma_32x32x16(ones, pb0, acc_l);
+            acc_l = mfma_32x32x16(ones, pb1, acc_l);
 
             const char *vt = st + pf::kKBytes + (lane & 31) * pf::kVStride + (kb + 4 * jj) * 2;
 #pragma unroll
@@ -237,12 +253,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
         }
         if (more) tile_store(r, smem + ((t + 1) & 1) * pf::kStage, tid);
         __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) slot1[i] = slot2[i];
     }
 
-    l += __shfl_xor(l, 32);
     lt += __shfl_xor(lt, 32);
     if (valid) {
-        const float inv = 1.0f / l;
+        const float inv = 1.0f / acc_l[0];
         bf16_t *op = reinterpret_cast<bf16_t *>(a.out) + ((int64_t)(row0 + tl) * a.q_heads + hq) * pf::kD;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
