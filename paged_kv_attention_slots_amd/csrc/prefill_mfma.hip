@@ -9,8 +9,8 @@
 // columns.  Keys stream through LDS in tiles of 64, double-buffered, with the
 // gathers pipelined: page-table slot ids are read two tiles ahead and the
 // 256-byte K and V rows of the next tile are in flight while the current tile
-// computes.  K is stored row-major; V is
-// stored transposed (dims x keys) so that it can feed the A operand below.
+// computes.  K and V tiles are stored row-major; V feeds the A operand below
+// through gfx950's transposing LDS read.
 //
 // Per 32 keys a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (A = 32 keys x 16 dims from LDS, B = Q^T held in registers, 8 steps over
@@ -18,8 +18,9 @@
 // one column; after the softmax update they are rounded to bf16 and are,
 // unchanged, the B operand (P^T) of O^T += V^T P^T, because the order of the
 // contraction index inside an MFMA is free as long as both operands agree:
-// the V^T reads pick the keys in the order the scores arrived in.  Nothing is
-// shuffled between lanes except one exchange for the column max.
+// the V^T reads (ds_read_b64_tr_b16 on the row-major V tile) pick the keys in
+// the order the scores arrived in.  Nothing is shuffled between lanes except
+// one exchange for the column max.
 //
 // Softmax: log2 domain (scale times log2 e folded into one fma before exp2),
 // running max per column and lazy rescaling: the output is only rescaled when
@@ -46,19 +47,15 @@ constexpr int kWaves = 4;
 constexpr int kColsW = 32;                     // query columns per wave
 constexpr int kCols = kWaves * kColsW;         // query columns per block
 constexpr int kKStride = kD * 2 + 16;          // bytes per key row of the K tile (padded)
-constexpr int kVStride = (kKT + 4) * 2;        // bytes per dim row of the V^T tile (padded)
+constexpr int kVStride = kD * 2 + 32;          // bytes per key row of the V tile (padded)
 constexpr int kKBytes = kKT * kKStride;
-constexpr int kVBytes = kD * kVStride;
+constexpr int kVBytes = kKT * kVStride;
 constexpr int kStage = kKBytes + kVBytes;
 constexpr float kRescaleLog2 = 8.0f;
 }  // namespace pf
 
 MSGL_DEV floatx16_t mfma_32x32x16(const bf16x8_t &a, const bf16x8_t &b, const floatx16_t &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-MSGL_DEV uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
-    return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }
 
 // A tile's gathers for one thread: keys 4*grp .. 4*grp+3, dims 8*sl .. 8*sl+7.
@@ -94,24 +91,26 @@ MSGL_DEV void tile_fetch(TileRegs &r, const int (&slot)[4], const bf16_t *__rest
     }
 }
 
-MSGL_DEV uint32_t comp(const uint4 &v, int p) { return p == 0 ? v.x : p == 1 ? v.y : p == 2 ? v.z : v.w; }
-
 MSGL_DEV void tile_store(const TileRegs &r, char *stage, int tid) {
     const int grp = tid >> 4;
     const int sl = tid & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
         *reinterpret_cast<uint4 *>(stage + (4 * grp + i) * pf::kKStride + sl * 16) = r.k[i];
-    char *vt = stage + pf::kKBytes;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t w0 = comp(r.v[0], p), w1 = comp(r.v[1], p), w2 = comp(r.v[2], p), w3 = comp(r.v[3], p);
-        // dim 8*sl + 2p: the low halves of the 4 keys; dim 8*sl + 2p + 1: the high halves
-        const uint2 lo = make_uint2(perm_b32(w1, w0, 0x05040100u), perm_b32(w3, w2, 0x05040100u));
-        const uint2 hi = make_uint2(perm_b32(w1, w0, 0x07060302u), perm_b32(w3, w2, 0x07060302u));
-        *reinterpret_cast<uint2 *>(vt + (sl * 8 + 2 * p) * pf::kVStride + grp * 8) = lo;
-        *reinterpret_cast<uint2 *>(vt + (sl * 8 + 2 * p + 1) * pf::kVStride + grp * 8) = hi;
+        *reinterpret_cast<uint4 *>(stage + pf::kKBytes + (4 * grp + i) * pf::kVStride + sl * 16) = r.v[i];
     }
+}
+
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane 4j+a names 4 consecutive 16-bit values; lane l receives value l%4 of
+// the lanes l/4, 4+l/4, 8+l/4 and 12+l/4.  When lanes 4j..4j+3 point at key
+// j's row at dims +0, +4, +8, +12, lane l therefore gets dim l of keys 0..3.
+MSGL_DEV uint2 lds_read_tr16(const char *p) {
+    const shortx4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) shortx4_t *)(const_cast<char *>(p)));
+    return __builtin_bit_cast(uint2, v);
 }
 
 template <int GQ>
@@ -189,14 +188,21 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
         if (more) tile_fetch(r, slot1, kh, vh, row_elems, num_slots, tid);
         const int k0 = t * pf::kKT;
         const bool need_mask = k0 + pf::kKT - 1 > pos0;
+        // scores of both 32-key halves first, so that the second half's MFMAs
+        // (and then the first half's P.V) overlap the softmax arithmetic
+        floatx16_t sc[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            sc[half] = floatx16_t{};
+            const char *krow = st + (half * 32 + (lane & 31)) * pf::kKStride + 16 * jj;
+#pragma unroll
+            for (int dc = 0; dc < 8; ++dc)
+                sc[half] = mfma_32x32x16(*reinterpret_cast<const bf16x8_t *>(krow + 32 * dc), qv[dc], sc[half]);
+        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int kb = half * 32;
-            floatx16_t s = floatx16_t{};
-            const char *krow = st + (kb + (lane & 31)) * pf::kKStride + 16 * jj;
-#pragma unroll
-            for (int dc = 0; dc < 8; ++dc)
-                s = mfma_32x32x16(*reinterpret_cast<const bf16x8_t *>(krow + 32 * dc), qv[dc], s);
+            floatx16_t &s = sc[half];
 
             // column max of the raw scores (the scale is positive), masked keys excluded
             if (need_mask) {
@@ -237,14 +243,17 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
             acc_l = mfma_32x32x16(ones, pb0, acc_l);
             acc_l = mfma_32x32x16(ones, pb1, acc_l);
 
-            const char *vt = st + pf::kKBytes + (lane & 31) * pf::kVStride + (kb + 4 * jj) * 2;
+            // V^T operands straight from the row-major V tile: lane L reads the
+            // rows of keys kb + 16*mm + 4*jj + (L/4)%4 (+8), dims 16*((L/16)%2) + 4*(L%4)
+            const char *vt = st + pf::kKBytes + (kb + 4 * jj + ((lane >> 2) & 3)) * pf::kVStride +
+                             (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
-                const char *vrow = vt + db * 32 * pf::kVStride;
-                const uint2 a0 = *reinterpret_cast<const uint2 *>(vrow);
-                const uint2 a1 = *reinterpret_cast<const uint2 *>(vrow + 16);
-                const uint2 a2 = *reinterpret_cast<const uint2 *>(vrow + 32);
-                const uint2 a3 = *reinterpret_cast<const uint2 *>(vrow + 48);
+                const char *vrow = vt + db * 32 * 2;
+                const uint2 a0 = lds_read_tr16(vrow);
+                const uint2 a1 = lds_read_tr16(vrow + 8 * pf::kVStride);
+                const uint2 a2 = lds_read_tr16(vrow + 16 * pf::kVStride);
+                const uint2 a3 = lds_read_tr16(vrow + 24 * pf::kVStride);
                 acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y)), pb0,
                                         acc[db]);
                 acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(a2.x, a2.y, a3.x, a3.y)), pb1,
