@@ -31,6 +31,43 @@ import time
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILE_DIR, "decode_attn_qwen3_8b_bs256_traffic.txt")
+# sources that define the decode attention kernels (a counter summary is only
+# valid for the sources it was taken on)
+DECODE_SOURCES = ("paged_kv_attention_slots_amd/csrc/decode.hip",
+                  "paged_kv_attention_slots_amd/csrc/attend_valu.h",
+                  "paged_kv_attention_slots_amd/csrc/common.h",
+                  "paged_kv_attention_slots_amd/csrc/launch.h")
+
+
+def decode_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode-attention launch from the committed counter summary,
+    or None when it is missing or was taken on other kernel sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_hash") != decode_source_hash():
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -60,7 +97,102 @@ def prefill_flops(w) -> float:
     return 4.0 * w.head_dim * w.q_heads * pairs
 
 
+def _read_csv(path):
+    import csv
+
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirname, suffix):
+    for root, _, files in os.walk(dirname):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirname}")
+
+
+def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes):
+    """Write the committed text summaries from rocprofv3 output directories:
+    the kernel-trace statistics of the bench command, and the decode kernels'
+    HBM bytes per launch from FETCH_SIZE / WRITE_SIZE runs, scaled by what the
+    same counters read for the plain copy kernel (torch.neg over a known size)."""
+    stats = _read_csv(_find(stats_dir, "kernel_stats.csv"))
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    lines = ["# rocprofv3 --kernel-trace --stats summary of the benchmark command",
+             f"# command: rocprofv3 --kernel-trace --stats --output-format csv -- {command}",
+             "# workload: Qwen3-8B decode bs 256 page_size 1 (graph + eager decode-attention launches),",
+             "#           ragged prefill 8 requests (Qwen3-0.6B heads); durations in microseconds", ""]
+    head = f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_%':>8}  kernel"
+    mine = [r for r in stats if "msgl::" in r["Name"]]
+    other = [r for r in stats if "msgl::" not in r["Name"]]
+
+    def row(r):
+        name = r["Name"].replace('"', "")
+        return (f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}  {name[:110]}")
+    lines += ["## library kernels", head] + [row(r) for r in mine]
+    lines += ["", "## largest other kernels (seeded input generation, torch copies)", head]
+    lines += [row(r) for r in other[:6]]
+    with open(os.path.join(PROFILE_DIR, "step_qwen3_8b_decode_bs256_ragged_prefill_kernel_stats.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_dispatch(dirname, counter):
+        rows = _read_csv(_find(dirname, "counter_collection.csv"))
+        out = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)  # KiB -> B
+        return out
+
+    fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = per_dispatch(write_dir, "WRITE_SIZE")
+
+    def one(d, key):
+        names = [n for n in d if key in n]
+        if not names:
+            raise KeyError(key)
+        vals = d[names[0]]
+        return sum(vals) / len(vals), len(vals)
+
+    neg_f, _ = one(fetch, "neg_kernel")
+    neg_w, _ = one(write, "neg_kernel")
+    cal = float(1 << 30)  # the bench negates 1 GiB (--copy-calibration-gib 1): 1 GiB read, 1 GiB written
+    f_scale, w_scale = cal / neg_f, cal / neg_w
+    split_f, n_split = one(fetch, "decode_split_kernel")
+    split_w, _ = one(write, "decode_split_kernel")
+    merge_f, _ = one(fetch, "decode_merge_kernel")
+    merge_w, _ = one(write, "decode_merge_kernel")
+    traffic = (split_f + merge_f) * f_scale + (split_w + merge_w) * w_scale
+    lines = [
+        "# HBM traffic of one decode-attention launch (split + merge kernels), Qwen3-8B shape, bs 256",
+        f"# command (three runs): rocprofv3 --kernel-trace --stats | --pmc FETCH_SIZE | --pmc WRITE_SIZE "
+        f"-- {command}",
+        "# counters are per dispatch (KiB), averaged over the eager launches; each is scaled by",
+        "# (known bytes / counter reading) of a plain copy kernel: torch.neg over 1 GiB of fp32",
+        f"copy_fetch_scale = {f_scale:.4f}",
+        f"copy_write_scale = {w_scale:.4f}",
+        f"split_fetch_bytes = {split_f:.0f}",
+        f"split_write_bytes = {split_w:.0f}",
+        f"merge_fetch_bytes = {merge_f:.0f}",
+        f"merge_write_bytes = {merge_w:.0f}",
+        f"dispatches_averaged = {n_split}",
+        f"algorithmic_bytes_per_launch = {workload_bytes}",
+        f"traffic_bytes_per_launch = {traffic:.0f}",
+        f"traffic_over_algorithmic = {traffic / workload_bytes:.4f}",
+        f"source_hash = {decode_source_hash()}",
+    ]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main() -> int:
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
+        # bench.py --summarize-profiles STATS_DIR FETCH_DIR WRITE_DIR ALGO_BYTES "COMMAND"
+        summarize_profiles(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[6], int(sys.argv[5]))
+        return 0
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -227,7 +359,7 @@ def main() -> int:
         "prefill_tflops": round(prefill_tflops, 2),
         "prefill_frac_of_bf16_peak": round(prefill_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode attention (split + merge), eager, bs 256",
                      "bytes_per_launch": dbytes, "avg_launch_ms": round(attn_ms, 4)},
         "cpu_baseline": cpu,
