@@ -188,7 +188,81 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes)
     print("\n".join(lines))
 
 
+def _time_stream(fn, stream, iters, warm=3):
+    import torch
+
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(iters):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def sweep(iters: int) -> int:
+    """Secondary measurements (one JSON line each): the captured decode step at
+    every padded batch size for page sizes 1 and 16, padding runs, eager
+    decode attention, and prefill on the ragged and chunked shapes."""
+    import torch
+
+    from paged_kv_attention_slots_amd import _lib, runner, workloads as wl
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    for ps in (1, 16):
+        full = wl.qwen3_8b_decode(page_size=ps, device=dev)
+        runs = [(n, n) for n in wl.GRAPH_BATCH_SIZES] + [(3, 4), (100, 128), (200, 256)]
+        for real, padded in runs:
+            w = wl.pad_decode(wl.subset_decode(full, real), padded)
+            out = torch.empty_like(w.q)
+            lse = torch.empty(padded, w.q_heads, dtype=torch.float32, device=dev)
+            ws = _lib.decode_workspace(padded, w.q_heads, w.head_dim, w.max_seq_len, device=dev)
+            torch.cuda.synchronize()
+            g = _lib.msgl_decode_graph_create(w.k_pool, w.v_pool, w.k_new, w.v_new, w.out_loc, out, lse, w.q,
+                                              w.page_table, w.table_idx, w.seq_lens, w.max_seq_len, ws,
+                                              page_size=ps, stream=stream)
+            ms = _time_stream(lambda: g.launch(stream), stream, iters)
+            g.destroy()
+            real_w = wl.subset_decode(full, real)
+            byts = decode_bytes(real_w) + store_bytes(real_w)
+            print(json.dumps({"sweep": "decode_graph_step", "page_size": ps, "batch": real, "padded": padded,
+                              "ms": round(ms, 4), "GBs": round(byts / ms / 1e6, 1),
+                              "frac_hbm": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4),
+                              "req_tokens_per_s": round(real / ms * 1e3, 1),
+                              "context_tokens": int(real_w.seq_lens.sum())}), flush=True)
+        out = torch.empty_like(full.q)
+        ws = _lib.decode_workspace(full.bs, full.q_heads, full.head_dim, full.max_seq_len, device=dev)
+        ms = _time_stream(lambda: runner.decode_attn(full, full.k_pool, full.v_pool, out=out, workspace=ws,
+                                                     with_lse=False, stream=stream), stream, iters)
+        byts = decode_bytes(full)
+        print(json.dumps({"sweep": "decode_attn_eager", "page_size": ps, "batch": full.bs, "ms": round(ms, 4),
+                          "GBs": round(byts / ms / 1e6, 1), "frac_hbm": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}),
+              flush=True)
+        del full
+        torch.cuda.empty_cache()
+    cases = [("ragged_prefill_8req", wl.ragged_prefill(device=dev)),
+             ("chunked_prefill_2x2048_on_8192", wl.ragged_prefill(
+                 device=dev, n_req=2, e_lo=2048, e_hi=2048, c_lo=8192, c_hi=8192, num_slots=1 << 15,
+                 heads=wl.QWEN3_8B, seed=1005))]
+    for name, w in cases:
+        out = torch.empty_like(w.q)
+        ms = _time_stream(lambda: runner.prefill_attn(w, w.k_pool, w.v_pool, out=out, with_lse=False,
+                                                      stream=stream), stream, iters)
+        fl = prefill_flops(w)
+        print(json.dumps({"sweep": "prefill_attn", "case": name, "tokens": w.num_tokens,
+                          "context_tokens": int(w.seq_lens.sum()), "ms": round(ms, 4),
+                          "TFLOPs": round(fl / ms / 1e9, 1),
+                          "frac_bf16_peak": round(fl / ms / 1e9 / BF16_DENSE_PEAK_TFLOPS, 4)}), flush=True)
+    return 0
+
+
 def main() -> int:
+    if len(sys.argv) > 1 and sys.argv[1] == "--sweep":
+        return sweep(int(sys.argv[2]) if len(sys.argv) > 2 else 20)
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
         # bench.py --summarize-profiles STATS_DIR FETCH_DIR WRITE_DIR ALGO_BYTES "COMMAND"
         summarize_profiles(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[6], int(sys.argv[5]))
@@ -348,7 +422,7 @@ def main() -> int:
             "decode": {"batch": w4.bs, "q_heads": w4.q_heads, "kv_heads": w4.kv_heads,
                        "head_dim": w4.head_dim, "page_size": w4.page_size,
                        "context_tokens": int(w4.seq_lens.sum()), "max_len": int(w4.seq_lens.max()),
-                       "chunk": args.chunk or 256},
+                       "min_keys_per_block": args.chunk or 128},
             "prefill": {"requests": w3.bs, "q_heads": w3.q_heads, "kv_heads": w3.kv_heads,
                         "head_dim": w3.head_dim, "extend_tokens": w3.num_tokens,
                         "context_tokens": int(w3.seq_lens.sum())},
