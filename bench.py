@@ -260,7 +260,54 @@ def sweep(iters: int) -> int:
     return 0
 
 
+def mixed(iters: int) -> int:
+    """The mixed multi-layer step (36 layers, 192 decode requests + 2 chunked
+    prefills of 2048 on 8192-token prefixes, pool 60% of 288 GB), eager, per
+    layer store_kv -> decode -> prefill.  One JSON line."""
+    import torch
+
+    from paged_kv_attention_slots_amd import _lib, workloads as wl
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    log("building the mixed step (36 layers, pool 60% of 288 GB)")
+    m = wl.mixed_step(device=dev)
+    torch.cuda.synchronize()
+    log(f"  built in {time.time() - t0:.1f}s")
+    stream = torch.cuda.Stream(device=dev)
+    d0, p0 = m.layer_views(0)
+    od = torch.empty_like(d0.q)
+    op = torch.empty_like(p0.q)
+    ws = _lib.decode_workspace(d0.bs, d0.q_heads, d0.head_dim, d0.max_seq_len, device=dev)
+    max_ext = int((p0.seq_lens - p0.cached_lens).max())
+    views = [m.layer_views(layer) for layer in range(m.layers)]
+
+    def step():
+        for d, p in views:
+            _lib.msgl_store_kv(d.k_pool, d.v_pool, m.k_new[d.layer], m.v_new[d.layer], m.out_loc, stream=stream)
+            _lib.msgl_decode_attn(od, None, d.q, d.k_pool, d.v_pool, d.page_table, d.table_idx, d.seq_lens,
+                                  d.max_seq_len, ws, stream=stream)
+            _lib.msgl_prefill_attn(op, None, p.q, p.k_pool, p.v_pool, p.page_table, p.table_idx, p.seq_lens,
+                                   p.cached_lens, p.cu_q, max_ext, stream=stream)
+
+    ms = _time_stream(step, stream, iters, warm=2)
+    dbytes = decode_bytes(d0) * m.layers
+    sbytes = (2 * 2 * m.num_tokens * d0.kv_heads * d0.head_dim * 2 + 4 * m.num_tokens) * m.layers
+    flops = prefill_flops(p0) * m.layers
+    roof_ms = ((dbytes + sbytes) / (HBM_PEAK_GBS * 1e9) + flops / (BF16_DENSE_PEAK_TFLOPS * 1e12)) * 1e3
+    print(json.dumps({"mixed_step": "qwen3-8b 36 layers: 192 decode + 2x2048 prefill on 8192 prefix",
+                      "ms_per_step": round(ms, 3), "tokens_per_step": m.num_tokens,
+                      "tokens_per_s": round(m.num_tokens / ms * 1e3, 1),
+                      "roofline_ms": round(roof_ms, 3), "frac_of_roofline": round(roof_ms / ms, 4),
+                      "decode_bytes": dbytes, "store_bytes": sbytes, "prefill_flops": flops,
+                      "slots_per_layer": d0.num_slots, "decode_context_tokens": int(d0.seq_lens.sum())}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
+    if len(sys.argv) > 1 and sys.argv[1] == "--mixed":
+        return mixed(int(sys.argv[2]) if len(sys.argv) > 2 else 5)
     if len(sys.argv) > 1 and sys.argv[1] == "--sweep":
         return sweep(int(sys.argv[2]) if len(sys.argv) > 2 else 20)
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":

@@ -508,3 +508,131 @@ def pad_decode(w: Workload, padded_bs: int) -> Workload:
         v_new=cat(w.v_new, torch.zeros(extra, w.kv_heads, w.head_dim, dtype=w.dtype, device=dev)),
         q=cat(w.q, torch.zeros(extra, w.q_heads, w.head_dim, dtype=w.dtype, device=dev)),
     )
+
+
+# ----------------------------------------------------------------------------
+# the mixed multi-layer step
+# ----------------------------------------------------------------------------
+
+MIXED_POOL_FRACTION = 0.6
+MIXED_HBM_BYTES = 288e9
+
+
+@dataclasses.dataclass
+class MixedStep:
+    """One engine step over `layers` layers: decode requests plus chunked
+    prefills in one batch.  All layers share the page table and metadata (one
+    free list, the same slots in every layer); each layer has its own pools,
+    new K/V rows and queries.  `decode` and `prefill` are per-layer workload
+    views (layer 0 here); `layer_inputs(l)` returns layer l's tensors."""
+    decode: Workload
+    prefill: Workload
+    layers: int
+    k_pools: List[torch.Tensor]
+    v_pools: List[torch.Tensor]
+    k_new: List[torch.Tensor]      # [T_decode + T_prefill, G, d] per layer
+    v_new: List[torch.Tensor]
+    q: List[torch.Tensor]          # [T_decode + T_prefill, H, d] per layer
+    out_loc: torch.Tensor          # [T_decode + T_prefill]
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.out_loc.numel())
+
+    def layer_views(self, layer: int):
+        """(decode, prefill) workload views bound to one layer's tensors."""
+        nd = self.decode.num_tokens
+        d = dataclasses.replace(self.decode, k_pool=self.k_pools[layer], v_pool=self.v_pools[layer],
+                                k_new=self.k_new[layer][:nd], v_new=self.v_new[layer][:nd],
+                                q=self.q[layer][:nd], layer=layer)
+        p = dataclasses.replace(self.prefill, k_pool=self.k_pools[layer], v_pool=self.v_pools[layer],
+                                k_new=self.k_new[layer][nd:], v_new=self.v_new[layer][nd:],
+                                q=self.q[layer][nd:], layer=layer)
+        return d, p
+
+
+def mixed_step(seed: int = 1005, device="cpu", layers: int = 36, n_decode: int = 192,
+               n_chunks: int = 2, chunk: int = 2048, prefix: int = 8192,
+               num_slots: Optional[int] = None, median: float = 2048.0, hi: int = 32768,
+               heads=QWEN3_8B, dtype: torch.dtype = torch.bfloat16) -> MixedStep:
+    """The mixed step: `n_decode` decode requests (lognormal contexts as in the
+    Qwen3-8B decode workload) and `n_chunks` chunked prefills of `chunk` new
+    tokens on a `prefix`-token cached prefix, over `layers` layers of Qwen3-8B
+    attention shapes.  The pool holds 60% of 288 GB (decimal) across all layers
+    at page_size 1: 0.6 * 288e9 / (layers * 2 * kv_heads * head_dim * 2 bytes)
+    slots per layer; one shuffled free list serves every layer."""
+    H, G, d = heads["H"], heads["G"], heads["d"]
+    e = torch.finfo(dtype).bits // 8
+    if num_slots is None:
+        num_slots = int(MIXED_POOL_FRACTION * MIXED_HBM_BYTES) // (layers * 2 * G * d * e)
+    rng = np.random.default_rng(seed)
+    dec_lens = lognormal_lengths(rng, n_decode, median=median, hi=hi)
+    free = rng.permutation(num_slots)
+    # decode requests: history then their new token; chunks: prefix then new tokens
+    dec_rows = rows_from_free_slots(free, dec_lens)
+    used = int(dec_lens.sum())
+    pre_lens = np.full(n_chunks, prefix + chunk, dtype=np.int64)
+    pre_rows = rows_from_free_slots(free[used:], pre_lens, new_after_history=False)
+    R = n_decode + n_chunks
+    W = align_up_32(max(hi, prefix + chunk))
+    pt = torch.zeros(R + 1, W, dtype=torch.int32)
+    for b, row in enumerate(dec_rows + pre_rows):
+        pt[b, :row.size] = torch.from_numpy(np.asarray(row).astype(np.int32))
+    pt[R, :] = num_slots
+    dec_cached = [int(L) - 1 for L in dec_lens]
+    pre_cached = [prefix] * n_chunks
+    lens = [int(x) for x in dec_lens] + [int(x) for x in pre_lens]
+    cached = dec_cached + pre_cached
+    tix = list(range(R))
+    # logical tokens of the whole step (decode requests first)
+    Ls = np.asarray(lens, dtype=np.int64)
+    tok_base = np.zeros(R + 1, dtype=np.int64)
+    tok_base[1:] = np.cumsum(Ls)
+    rows_all = dec_rows + pre_rows
+    hist_tok = torch.from_numpy(np.concatenate([tok_base[b] + np.arange(cached[b]) for b in range(R)]))
+    hist_slot = torch.from_numpy(np.concatenate([np.asarray(rows_all[b][:cached[b]], dtype=np.int64)
+                                                 for b in range(R)]))
+    new_tok = torch.from_numpy(np.concatenate([tok_base[b] + np.arange(cached[b], lens[b]) for b in range(R)]))
+
+    def meta(sel):
+        t_idx = torch.tensor([tix[b] for b in sel], dtype=torch.int32)
+        s = torch.tensor([lens[b] for b in sel], dtype=torch.int32)
+        c = torch.tensor([cached[b] for b in sel], dtype=torch.int32)
+        cu, pos, loc = _build_metadata(pt, t_idx, s, c)
+        return t_idx, s, c, cu, pos, loc
+
+    k_pools, v_pools, k_news, v_news, qs = [], [], [], [], []
+    for layer in range(layers):
+        kp, vp, kn, vn, q = _fill(seed, layer, hist_slot, hist_tok, new_tok, int(new_tok.numel()), G, H, d,
+                                  dtype, 1.0, 1.0 / math.sqrt(128), num_slots + 1, device)
+        k_pools.append(kp)
+        v_pools.append(vp)
+        k_news.append(kn)
+        v_news.append(vn)
+        qs.append(q)
+    views = []
+    nd_tokens = n_decode
+    for sel, mode, sl in ((range(n_decode), "decode", slice(0, nd_tokens)),
+                          (range(n_decode, R), "prefill", slice(nd_tokens, None))):
+        t_idx, s, c, cu, pos, loc = meta(list(sel))
+        views.append(Workload(
+            name=f"mixed-{mode}", mode=mode, dtype=dtype, q_heads=H, kv_heads=G, head_dim=d, page_size=1,
+            num_slots=num_slots, max_running_req=R, max_seq_len=W, page_table=pt.to(device),
+            table_idx=t_idx.to(device), seq_lens=s.to(device), cached_lens=c.to(device), cu_q=cu.to(device),
+            positions=pos.to(device), out_loc=loc.to(device), k_pool=k_pools[0], v_pool=v_pools[0],
+            k_new=k_news[0][sl], v_new=v_news[0][sl], q=qs[0][sl], seed=seed, layer=0))
+    out_loc = torch.cat([views[0].out_loc, views[1].out_loc])
+    return MixedStep(decode=views[0], prefill=views[1], layers=layers, k_pools=k_pools, v_pools=v_pools,
+                     k_new=k_news, v_new=v_news, q=qs, out_loc=out_loc)
+
+
+def layer_history_values(step: MixedStep, layer: int, request: int, positions: torch.Tensor, which: str):
+    """Regenerate the K ('k') or V ('v') rows of one request's history positions
+    in one layer, as the generator placed them (for spot checks of pools)."""
+    w = step.decode if request < step.decode.bs else step.prefill
+    lens = torch.cat([step.decode.seq_lens.cpu(), step.prefill.seq_lens.cpu()]).long()
+    base = int(lens[:request].sum())
+    stream = (STREAM_K if which == "k" else STREAM_V) + 4 * layer
+    rows = base + positions.long().cpu()
+    return gen_rows(w.seed, stream, rows, w.kv_heads * w.head_dim, 1.0, w.dtype, "cpu").view(
+        -1, w.kv_heads, w.head_dim)
