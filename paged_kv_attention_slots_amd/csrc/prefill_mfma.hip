@@ -20,7 +20,7 @@
 // contraction index inside an MFMA is free as long as both operands agree:
 // the V^T reads (ds_read_b64_tr_b16 on the row-major V tile) pick the keys in
 // the order the scores arrived in.  Nothing is shuffled between lanes except
-// one exchange for the column max.
+// one exchange for the column max (v_permlane32_swap, no LDS round trip).
 //
 // Softmax: log2 domain (scale times log2 e folded into one fma before exp2),
 // running max per column and lazy rescaling: the output is only rescaled when
@@ -99,6 +99,19 @@ MSGL_DEV void tile_store(const TileRegs &r, char *stage, int tid) {
         *reinterpret_cast<uint4 *>(stage + (4 * grp + i) * pf::kKStride + sl * 16) = r.k[i];
         *reinterpret_cast<uint4 *>(stage + pf::kKBytes + (4 * grp + i) * pf::kVStride + sl * 16) = r.v[i];
     }
+}
+
+// Combine a value with the one held by lane l ^ 32 (v_permlane32_swap: after
+// swapping the upper half of a copy with the lower half of another copy, each
+// lane holds its own value in one result and its partner's in the other).
+MSGL_DEV float max_with_other_half(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+MSGL_DEV float add_with_other_half(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 typedef short shortx4_t __attribute__((ext_vector_type(4)));
@@ -190,62 +203,70 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
         const bool need_mask = k0 + pf::kKT - 1 > pos0;
         // scores of both 32-key halves first, so that the second half's MFMAs
         // (and then the first half's P.V) overlap the softmax arithmetic
-        floatx16_t sc[2];
+        floatx16_t sc[2] = {floatx16_t{}, floatx16_t{}};
+        {
+            const char *krow = st + (lane & 31) * pf::kKStride + 16 * jj;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            sc[half] = floatx16_t{};
-            const char *krow = st + (half * 32 + (lane & 31)) * pf::kKStride + 16 * jj;
+            for (int dc = 0; dc < 8; ++dc)  // two independent accumulation chains, interleaved
 #pragma unroll
-            for (int dc = 0; dc < 8; ++dc)
-                sc[half] = mfma_32x32x16(*reinterpret_cast<const bf16x8_t *>(krow + 32 * dc), qv[dc], sc[half]);
+                for (int half = 0; half < 2; ++half)
+                    sc[half] = mfma_32x32x16(
+                        *reinterpret_cast<const bf16x8_t *>(krow + half * 32 * pf::kKStride + 32 * dc), qv[dc],
+                        sc[half]);
         }
+        // causal mask, only on tiles that reach past the block's first position
+        if (need_mask) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int kb = half * 32;
-            floatx16_t &s = sc[half];
-
-            // column max of the raw scores (the scale is positive), masked keys excluded
-            if (need_mask) {
+            for (int half = 0; half < 2; ++half)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int key = k0 + kb + 8 * (e >> 2) + 4 * jj + (e & 3);
-                    s[e] = key > pos ? -INFINITY : s[e];
+                    const int key = k0 + half * 32 + 8 * (e >> 2) + 4 * jj + (e & 3);
+                    sc[half][e] = key > pos ? -INFINITY : sc[half][e];
                 }
-            }
-            float mx = s[0];
+        }
+        // one column max per 64-key tile (raw scores; the scale is positive)
+        float mx = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
-            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-            if (__any(mx > m + pf::kRescaleLog2)) {
-                const float mn = fmaxf(m, mx);
-                const float alpha = (mn == -INFINITY) ? 1.0f : fast_exp2(m - mn);
-                lt *= alpha;
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sc[0][e], sc[1][e]));
+        mx = max_with_other_half(mx) * a.scale_log2;
+        if (__any(mx > m + pf::kRescaleLog2)) {
+            const float mn = fmaxf(m, mx);
+            const float alpha = (mn == -INFINITY) ? 1.0f : fast_exp2(m - mn);
+            lt *= alpha;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc_l[e] *= alpha;
+            for (int e = 0; e < 16; ++e) acc_l[e] *= alpha;
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
-                m = mn;
-            }
-            const float nmu = (m == -INFINITY) ? 0.0f : -m;
+                for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+            m = mn;
+        }
+        const float nmu = (m == -INFINITY) ? 0.0f : -m;
+
+        // weights of both halves, then the row sums and P.V: one straight-line
+        // region, so the MFMAs of one half overlap the arithmetic of the other
+        bf16x8_t pb[2][2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
             uint32_t pw[8];
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-                const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, nmu));
-                const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, nmu));
+                const float p0 = fast_exp2(fmaf(sc[half][e], a.scale_log2, nmu));
+                const float p1 = fast_exp2(fmaf(sc[half][e + 1], a.scale_log2, nmu));
                 pw[e >> 1] = pack_bf16x2(p0, p1);
                 lt += p0 + p1;
             }
-            const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-            const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+            pb[half][0] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+            pb[half][1] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
             // running sum of the rounded weights: every row of ones . P^T is the column sum
-            acc_l = mfma_32x32x16(ones, pb0, acc_l);
-            acc_l = mfma_32x32x16(ones, pb1, acc_l);
-
+            acc_l = mfma_32x32x16(ones, pb[half][0], acc_l);
+            acc_l = mfma_32x32x16(ones, pb[half][1], acc_l);
             // V^T operands straight from the row-major V tile: lane L reads the
             // rows of keys kb + 16*mm + 4*jj + (L/4)%4 (+8), dims 16*((L/16)%2) + 4*(L%4)
-            const char *vt = st + pf::kKBytes + (kb + 4 * jj + ((lane >> 2) & 3)) * pf::kVStride +
+            const char *vt = st + pf::kKBytes + (half * 32 + 4 * jj + ((lane >> 2) & 3)) * pf::kVStride +
                              (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
@@ -254,10 +275,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
                 const uint2 a1 = lds_read_tr16(vrow + 8 * pf::kVStride);
                 const uint2 a2 = lds_read_tr16(vrow + 16 * pf::kVStride);
                 const uint2 a3 = lds_read_tr16(vrow + 24 * pf::kVStride);
-                acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y)), pb0,
-                                        acc[db]);
-                acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(a2.x, a2.y, a3.x, a3.y)), pb1,
-                                        acc[db]);
+                acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y)),
+                                        pb[half][0], acc[db]);
+                acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(a2.x, a2.y, a3.x, a3.y)),
+                                        pb[half][1], acc[db]);
             }
         }
         if (more) tile_store(r, smem + ((t + 1) & 1) * pf::kStage, tid);
@@ -266,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
         for (int i = 0; i < 4; ++i) slot1[i] = slot2[i];
     }
 
-    lt += __shfl_xor(lt, 32);
+    lt = add_with_other_half(lt);
     if (valid) {
         const float inv = 1.0f / acc_l[0];
         bf16_t *op = reinterpret_cast<bf16_t *>(a.out) + ((int64_t)(row0 + tl) * a.q_heads + hq) * pf::kD;
