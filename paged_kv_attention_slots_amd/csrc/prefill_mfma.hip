@@ -3,14 +3,17 @@
 // New token i of request b sits at position p = cached_len + i and attends
 // keys 0..p of its page-table row: a causal mask offset by the cached prefix.
 //
-// Block = one kv head x one block of query tokens.  Its 128 "columns" are
-// (token, q head) pairs of the q heads that share the kv head (token-major),
-// so every gathered K/V tile serves all of them.  Each of the 4 waves owns 32
-// columns.  Keys stream through LDS in tiles of 64, double-buffered, with the
-// gathers pipelined: page-table slot ids are read two tiles ahead and the
-// 256-byte K and V rows of the next tile are in flight while the current tile
-// computes.  K and V tiles are stored row-major; V feeds the A operand below
-// through gfx950's transposing LDS read.
+// Block = one kv head x 256 query "columns", one block per CU.  A column is a
+// (token, q head) pair of the q heads that share the kv head (token-major), so
+// every gathered K/V tile serves the whole group; each of the 8 waves owns 32
+// columns.  Keys stream through a ring of 4 LDS stages of 64 keys (K rows, then
+// V rows, 256 bytes each, their 16-byte chunks permuted per row so that the
+// column-wise reads below hit every bank once).  The gathers go straight from
+// the pools into LDS (global_load_lds_dwordx4: lane l's 16 bytes land at the
+// destination + 16 l), three tiles ahead of the compute; the page-table ids
+// are scalar loads five tiles ahead.  Every iteration issues the same four
+// vector memory instructions per wave, so one vmcnt wait plus one barrier per
+// tile is exact.
 //
 // Per 32 keys a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (A = 32 keys x 16 dims from LDS, B = Q^T held in registers, 8 steps over
@@ -18,18 +21,19 @@
 // one column; after the softmax update they are rounded to bf16 and are,
 // unchanged, the B operand (P^T) of O^T += V^T P^T, because the order of the
 // contraction index inside an MFMA is free as long as both operands agree:
-// the V^T reads (ds_read_b64_tr_b16 on the row-major V tile) pick the keys in
+// the V^T reads (ds_read_b64_tr_b16 on the row-major V rows) pick the keys in
 // the order the scores arrived in.  Nothing is shuffled between lanes except
 // one exchange for the column max (v_permlane32_swap, no LDS round trip).
 //
 // Softmax: log2 domain (scale times log2 e folded into one fma before exp2),
-// running max per column and lazy rescaling: the output is only rescaled when
-// a column's max grows by more than 2^8, which keeps exp2 arguments bounded
-// and skips almost every rescale.  The output is normalised by the sum of the
-// bf16-rounded probabilities that the P.V product uses, so the applied weights
-// sum to one; that sum is itself two more MFMAs (an all-ones A operand times
-// P^T gives the column sums in every row).  The returned lse comes from a
-// lane-partial fp32 sum of the unrounded weights, reduced once at the end.
+// one running max per column per 64-key tile and lazy rescaling: the output is
+// only rescaled when a column's max grows by more than 2^8, which keeps exp2
+// arguments bounded and skips almost every rescale.  The output is normalised
+// by the sum of the bf16-rounded probabilities that the P.V product uses, so
+// the applied weights sum to one; that sum is itself two more MFMAs (an
+// all-ones A operand times P^T gives the column sums in every row).  The
+// returned lse comes from a lane-partial fp32 sum of the unrounded weights,
+// reduced once at the end.
 //
 // Blocks are ordered longest-first (last query blocks, which see the most
 // keys, get the lowest block ids) so the ragged tail balances.
@@ -39,66 +43,26 @@
 namespace msgl {
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
 
 namespace pf {
 constexpr int kD = 128;
-constexpr int kKT = 64;                        // keys per LDS tile
-constexpr int kWaves = 4;
-constexpr int kColsW = 32;                     // query columns per wave
-constexpr int kCols = kWaves * kColsW;         // query columns per block
-constexpr int kKStride = kD * 2 + 16;          // bytes per key row of the K tile (padded)
-constexpr int kVStride = kD * 2 + 32;          // bytes per key row of the V tile (padded)
-constexpr int kKBytes = kKT * kKStride;
-constexpr int kVBytes = kKT * kVStride;
-constexpr int kStage = kKBytes + kVBytes;
+constexpr int kKT = 64;                    // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kColsW = 32;                 // query columns per wave
+constexpr int kCols = kWaves * kColsW;     // query columns per block
+constexpr int kRow = kD * 2;               // bytes per K or V row in LDS
+constexpr int kHalf = kKT * kRow;          // the K rows of a stage, then its V rows
+constexpr int kStage = 2 * kHalf;
+constexpr int kStages = 4;
+constexpr int kAhead = kStages - 1;        // tiles gathered ahead of the compute
+constexpr int kGathersPerTile = 4;         // vector memory instructions per wave per tile
 constexpr float kRescaleLog2 = 8.0f;
 }  // namespace pf
 
 MSGL_DEV floatx16_t mfma_32x32x16(const bf16x8_t &a, const bf16x8_t &b, const floatx16_t &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// A tile's gathers for one thread: keys 4*grp .. 4*grp+3, dims 8*sl .. 8*sl+7.
-struct TileRegs {
-    uint4 k[4];
-    uint4 v[4];
-};
-
-// Slot ids of a thread's 4 keys in the tile starting at k0 (-1 past nkeys).
-MSGL_DEV void tile_slots(int (&slot)[4], const int32_t *__restrict__ pt, int k0, int nkeys, int tid) {
-    const int grp = tid >> 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 4 * grp + i;
-        slot[i] = key < nkeys ? pt[key] : -1;
-    }
-}
-
-MSGL_DEV void tile_fetch(TileRegs &r, const int (&slot)[4], const bf16_t *__restrict__ kh,
-                         const bf16_t *__restrict__ vh, int64_t row_elems, uint32_t num_slots, int tid) {
-    const int sl = tid & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (slot[i] >= 0) {
-            const int64_t s = (uint32_t)slot[i] < num_slots ? slot[i] : 0;  // malformed id: stay in the pool
-            const int64_t off = s * row_elems + sl * 8;
-            r.k[i] = ld16(kh + off);
-            r.v[i] = ld16(vh + off);
-        } else {
-            r.k[i] = make_uint4(0, 0, 0, 0);  // keys past the end: zero rows (masked anyway)
-            r.v[i] = make_uint4(0, 0, 0, 0);
-        }
-    }
-}
-
-MSGL_DEV void tile_store(const TileRegs &r, char *stage, int tid) {
-    const int grp = tid >> 4;
-    const int sl = tid & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4 *>(stage + (4 * grp + i) * pf::kKStride + sl * 16) = r.k[i];
-        *reinterpret_cast<uint4 *>(stage + pf::kKBytes + (4 * grp + i) * pf::kVStride + sl * 16) = r.v[i];
-    }
 }
 
 // Combine a value with the one held by lane l ^ 32 (v_permlane32_swap: after
@@ -114,8 +78,6 @@ MSGL_DEV float add_with_other_half(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-typedef short shortx4_t __attribute__((ext_vector_type(4)));
-
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane 4j+a names 4 consecutive 16-bit values; lane l receives value l%4 of
 // the lanes l/4, 4+l/4, 8+l/4 and 12+l/4.  When lanes 4j..4j+3 point at key
@@ -126,14 +88,65 @@ MSGL_DEV uint2 lds_read_tr16(const char *p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// Row permutation code: chunk c of row r sits at chunk position c ^ code(r).
+// code is a bijection on r % 16, so 16 (or 8) consecutive rows read at one
+// chunk spread over all positions (the K reads), and its bits 1..3 give 4
+// consecutive rows distinct chunk groups (the transposing V reads, 4 chunks
+// of 4 rows at once).
+MSGL_DEV int row_code(int r) {
+    return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r ^ (r >> 3)) & 1) << 3);
+}
+
+// The 8 page-table ids of rows 8w..8w+7 of a tile (uniform per wave, scalar
+// loads, left unchecked until they are used).  Keys past the block's last one
+// read key 0's id: a real row whose scores the causal mask removes.
+typedef int TileIds __attribute__((ext_vector_type(8)));
+
+MSGL_DEV void load_ids(TileIds &ids, const __attribute__((address_space(4))) int32_t *pt, int key0, int nkeys) {
+    if (key0 + 8 <= nkeys) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ids[j] = pt[key0 + j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ids[j] = pt[key0 + j < nkeys ? key0 + j : 0];
+    }
+}
+
+// One gather of 16 bytes per lane straight into LDS (global_load_lds_dwordx4):
+// lane l's bytes land at LDS address lds + 16 l (lds is wave-uniform, in M0).
+// Issued as inline assembly so that the compiler neither counts it nor holds
+// later LDS reads back for it: the kernel orders it itself (vmcnt + barrier).
+MSGL_DEV void gather_to_lds(const void *src, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// Gathers of one tile by one wave to LDS address `dst` (the stage + this
+// wave's first row): K rows then V rows 8w + 4i + l/16 (i = 0, 1).  Lane l
+// writes chunk position l%16 of its row, so gofs names the chunk the row
+// permutation puts there.
+MSGL_DEV void issue_tile(uint32_t dst, TileIds ids, int grp, const char *kbase, int64_t v_minus_k, int64_t row_bytes,
+                         uint2 gofs, uint32_t num_slots) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        int s = ids[4 * i];
+        s = grp == 1 ? ids[4 * i + 1] : s;
+        s = grp == 2 ? ids[4 * i + 2] : s;
+        s = grp == 3 ? ids[4 * i + 3] : s;
+        s = (uint32_t)s < num_slots ? s : 0;  // a malformed id stays inside the pool
+        const char *ksrc = kbase + (int64_t)s * row_bytes + (i == 0 ? gofs.x : gofs.y);
+        gather_to_lds(ksrc, dst + 4 * i * pf::kRow);
+        gather_to_lds(ksrc + v_minus_k, dst + pf::kHalf + 4 * i * pf::kRow);
+    }
+}
+
 template <int GQ>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int nqb) {
+__global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillArgs a, int nqb) {
     constexpr int BQ = pf::kCols / GQ;  // query tokens per block
-    __shared__ __attribute__((aligned(16))) char smem[2 * pf::kStage];
+    __shared__ __attribute__((aligned(1024))) char smem[pf::kStages * pf::kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int jj = lane >> 5;
     const int G = a.kv_heads;
 
@@ -153,6 +166,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
     if (ntok <= 0) return;
     const int pos0 = C + t0;         // position of the block's first token
     const int nkeys = pos0 + ntok;   // keys 0 .. position of its last token
+    const int ntiles = (nkeys + pf::kKT - 1) / pf::kKT;
 
     // this lane's query column
     const int col = wave * pf::kColsW + (lane & 31);
@@ -161,13 +175,41 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
     const bool valid = tl < ntok;
     const int tok = valid ? tl : ntok - 1;
     const int pos = pos0 + tok;
+    // the wave's last position: tiles that start beyond it are skipped by this wave
+    const int wave_last = pos0 + min((wave * pf::kColsW + pf::kColsW - 1) / GQ, ntok - 1);
 
-    // Q^T operands: d-chunk dc holds dims 16*dc + 8*jj .. +7 of this column
+    // gather sources: page-table row, pools at this kv head, per-lane chunk offsets
+    const auto *pt = (const __attribute__((address_space(4))) int32_t *)(
+        a.page_table + (int64_t)a.table_idx[b] * a.row_stride);
+    const uint32_t num_slots = (uint32_t)a.num_slots;
+    const int64_t row_bytes = (int64_t)G * pf::kD * 2;
+    const char *kbase = reinterpret_cast<const char *>(a.k_pool) + (int64_t)kvh * pf::kRow;
+    const int64_t v_minus_k = reinterpret_cast<const char *>(a.v_pool) - reinterpret_cast<const char *>(a.k_pool);
+    const int grp = lane >> 4;
+    const uint32_t lds_wave = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem +
+                              8 * wave * pf::kRow;  // this wave's first row of stage 0
+    const uint2 gofs = make_uint2(((lane & 15) ^ row_code(8 * wave + grp)) << 4,
+                                  ((lane & 15) ^ row_code(8 * wave + 4 + grp)) << 4);
+
+    // pipeline prologue: gathers of tiles 0..2, then Q, then the ids of tiles 3 and 4
+    TileIds ids3, ids4;
+#pragma unroll
+    for (int t = 0; t < pf::kAhead; ++t) {
+        load_ids(ids3, pt, t * pf::kKT + 8 * wave, nkeys);
+        issue_tile(lds_wave + t * pf::kStage, ids3, grp, kbase, v_minus_k, row_bytes, gofs, num_slots);
+    }
+    // Q^T operands: d-chunk dc holds dims 16*dc + 8*jj .. +7 of this column.
+    // The empty asm below makes the compiler wait for them here, once; the
+    // gathers it cannot see are older, so they are complete then as well.
     bf16x8_t qv[8];
     const bf16_t *qp = reinterpret_cast<const bf16_t *>(a.q) +
                        ((int64_t)(row0 + tok) * a.q_heads + hq) * pf::kD + 8 * jj;
 #pragma unroll
     for (int dc = 0; dc < 8; ++dc) qv[dc] = __builtin_bit_cast(bf16x8_t, ld16(qp + 16 * dc));
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) asm volatile("" ::"v"(qv[dc]));
+    load_ids(ids3, pt, 3 * pf::kKT + 8 * wave, nkeys);
+    load_ids(ids4, pt, 4 * pf::kKT + 8 * wave, nkeys);
 
     floatx16_t acc[4];
 #pragma unroll
@@ -178,42 +220,48 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
     const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u,
                                                                   0x3f803f80u));
 
-    const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
-    const bf16_t *kh = reinterpret_cast<const bf16_t *>(a.k_pool) + (int64_t)kvh * pf::kD;
-    const bf16_t *vh = reinterpret_cast<const bf16_t *>(a.v_pool) + (int64_t)kvh * pf::kD;
-    const int64_t row_elems = (int64_t)G * pf::kD;
-    const uint32_t num_slots = (uint32_t)a.num_slots;
-    const int ntiles = (nkeys + pf::kKT - 1) / pf::kKT;
-
-    // pipeline: slot ids two tiles ahead, K/V rows one tile ahead, LDS double-buffered
-    TileRegs r;
-    int slot0[4], slot1[4], slot2[4];
-    tile_slots(slot0, pt, 0, nkeys, tid);
-    tile_slots(slot1, pt, pf::kKT, nkeys, tid);
-    tile_fetch(r, slot0, kh, vh, row_elems, num_slots, tid);
-    tile_store(r, smem, tid);
-    __syncthreads();
+    // LDS read offsets within a stage.  K (A of S^T): row (lane%32) [+32 for
+    // the second half], chunk 2*dc + jj.  V (A of O^T, transposing reads):
+    // lane L reads row 4*jj + (L/4)%4 [+8*qq, +32 for the second half] at
+    // dims 32*db + 16*((L/16)%2) + 4*(L%4), i.e. chunk 4*db + vch, byte 8*(L%2).
+    const int kx = row_code(lane & 15) ^ jj;
+    const int krow = (lane & 31) * pf::kRow;
+    const int vrow = 4 * jj + ((lane >> 2) & 3);
+    const int vch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int vx0 = vrow * pf::kRow + ((vch ^ row_code(vrow)) << 4) + (lane & 1) * 8;      // qq even
+    const int vx1 = vrow * pf::kRow + ((vch ^ row_code(vrow + 8)) << 4) + (lane & 1) * 8;  // qq odd
 
     for (int t = 0; t < ntiles; ++t) {
-        const char *st = smem + (t & 1) * pf::kStage;
-        const bool more = t + 1 < ntiles;
-        tile_slots(slot2, pt, (t + 2) * pf::kKT, nkeys, tid);
-        if (more) tile_fetch(r, slot1, kh, vh, row_elems, num_slots, tid);
-        const int k0 = t * pf::kKT;
-        const bool need_mask = k0 + pf::kKT - 1 > pos0;
-        // scores of both 32-key halves first, so that the second half's MFMAs
-        // (and then the first half's P.V) overlap the softmax arithmetic
-        floatx16_t sc[2] = {floatx16_t{}, floatx16_t{}};
+        // this wave's gathers of tile t are done (the two later tiles' are
+        // still allowed in flight); after the barrier everyone's are, and every
+        // wave has finished reading tile t-1's stage
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        static_assert(2 * pf::kGathersPerTile == 8, "vmcnt above counts the gathers of two tiles");
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         {
-            const char *krow = st + (lane & 31) * pf::kKStride + 16 * jj;
-#pragma unroll
-            for (int dc = 0; dc < 8; ++dc)  // two independent accumulation chains, interleaved
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-                    sc[half] = mfma_32x32x16(
-                        *reinterpret_cast<const bf16x8_t *>(krow + half * 32 * pf::kKStride + 32 * dc), qv[dc],
-                        sc[half]);
+            TileIds ids5;
+            load_ids(ids5, pt, (t + 5) * pf::kKT + 8 * wave, nkeys);
+            issue_tile(lds_wave + ((t + pf::kAhead) % pf::kStages) * pf::kStage, ids3, grp, kbase, v_minus_k,
+                       row_bytes, gofs, num_slots);  // past the end: harmless reloads
+            ids3 = ids4;
+            ids4 = ids5;
         }
+        const int k0 = t * pf::kKT;
+        if (k0 > wave_last) continue;  // every key of the tile is masked for this wave
+        const char *st = smem + (t % pf::kStages) * pf::kStage;
+        const bool need_mask = k0 + pf::kKT - 1 > pos0;
+
+        // scores of both 32-key halves: two independent accumulation chains
+        floatx16_t sc[2] = {floatx16_t{}, floatx16_t{}};
+#pragma unroll
+        for (int dc = 0; dc < 8; ++dc)
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                sc[half] = mfma_32x32x16(
+                    *reinterpret_cast<const bf16x8_t *>(st + half * 32 * pf::kRow + krow + (((2 * dc) ^ kx) << 4)),
+                    qv[dc], sc[half]);
         // causal mask, only on tiles that reach past the block's first position
         if (need_mask) {
 #pragma unroll
@@ -224,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
                     sc[half][e] = key > pos ? -INFINITY : sc[half][e];
                 }
         }
-        // one column max per 64-key tile (raw scores; the scale is positive)
+        // one column max per tile (raw scores; the scale is positive)
         float mx = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sc[0][e], sc[1][e]));
@@ -259,33 +307,28 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
             pb[half][0] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
             pb[half][1] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
         }
+        const char *vs = st + pf::kHalf;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             // running sum of the rounded weights: every row of ones . P^T is the column sum
             acc_l = mfma_32x32x16(ones, pb[half][0], acc_l);
             acc_l = mfma_32x32x16(ones, pb[half][1], acc_l);
-            // V^T operands straight from the row-major V tile: lane L reads the
-            // rows of keys kb + 16*mm + 4*jj + (L/4)%4 (+8), dims 16*((L/16)%2) + 4*(L%4)
-            const char *vt = st + pf::kKBytes + (half * 32 + 4 * jj + ((lane >> 2) & 3)) * pf::kVStride +
-                             (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
-                const char *vrow = vt + db * 32 * 2;
-                const uint2 a0 = lds_read_tr16(vrow);
-                const uint2 a1 = lds_read_tr16(vrow + 8 * pf::kVStride);
-                const uint2 a2 = lds_read_tr16(vrow + 16 * pf::kVStride);
-                const uint2 a3 = lds_read_tr16(vrow + 24 * pf::kVStride);
-                acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y)),
+                uint2 av[4];
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+                    av[qq] = lds_read_tr16(vs + (half * 32 + 8 * qq) * pf::kRow +
+                                           ((qq & 1 ? vx1 : vx0) ^ (db << 6)));
+                acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(av[0].x, av[0].y, av[1].x, av[1].y)),
                                         pb[half][0], acc[db]);
-                acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(a2.x, a2.y, a3.x, a3.y)),
+                acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(av[2].x, av[2].y, av[3].x, av[3].y)),
                                         pb[half][1], acc[db]);
             }
         }
-        if (more) tile_store(r, smem + ((t + 1) & 1) * pf::kStage, tid);
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) slot1[i] = slot2[i];
     }
+    // the gathers issued past the last tile must land before the block's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     lt = add_with_other_half(lt);
     if (valid) {
@@ -313,7 +356,7 @@ hipError_t run_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     const int64_t grid = (int64_t)nqb * a.batch * a.kv_heads;
     if (grid < 1) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_mfma_kernel<GQ>), dim3((unsigned)grid), dim3(256), 0, stream, a, nqb);
+    hipLaunchKernelGGL((prefill_mfma_kernel<GQ>), dim3((unsigned)grid), dim3(pf::kThreads), 0, stream, a, nqb);
     return hipGetLastError();
 }
 
