@@ -6,19 +6,24 @@
 // Block = one kv head x 256 query "columns", one block per CU.  A column is a
 // (token, q head) pair of the q heads that share the kv head (token-major), so
 // every gathered K/V tile serves the whole group; each of the 8 waves owns 32
-// columns.  Keys stream through a ring of 4 LDS stages of 64 keys (K rows, then
-// V rows, 256 bytes each, their 16-byte chunks permuted per row so that the
+// columns.  Keys stream through a ring of 4 LDS stages of 64-key tiles (K rows
+// and V rows of 256 bytes, their 16-byte chunks permuted per row so that the
 // column-wise reads below hit every bank once).  The gathers go straight from
 // the pools into LDS (global_load_lds_dwordx4: lane l's 16 bytes land at the
-// destination + 16 l), three tiles ahead of the compute; the page-table ids
-// are scalar loads five tiles ahead.  Every iteration issues the same four
-// vector memory instructions per wave, so one vmcnt wait plus one barrier per
-// tile is exact.
+// destination + 16 l, so one instruction fills 4 rows), three tiles ahead of
+// the compute.  The page-table ids of a tile are copied into LDS the same way
+// two tiles before its gathers.  Every iteration issues the same five vector
+// memory instructions per wave, so one vmcnt wait plus one barrier per tile
+// is exact.  The main loop is unrolled over the 4 stages so that every LDS
+// read address is a per-lane register plus an immediate.
 //
-// Per 32 keys a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
-// (A = 32 keys x 16 dims from LDS, B = Q^T held in registers, 8 steps over
-// head_dim 128).  The MFMA result layout leaves each lane with 16 scores of
-// one column; after the softmax update they are rounded to bf16 and are,
+// Keys are processed in units of 32 (half a tile).  For unit u a wave
+// computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims
+// from LDS, B = Q^T held in registers, 8 steps over head_dim 128) two units
+// ahead of its P.V and its softmax one unit ahead, so that the MFMAs of a unit
+// (scores of u+2, P.V of u) and its VALU work (softmax of u+1) are independent
+// and overlap.  The MFMA result layout leaves each lane with 16 scores of one
+// column; after the softmax update they are rounded to bf16 and are,
 // unchanged, the B operand (P^T) of O^T += V^T P^T, because the order of the
 // contraction index inside an MFMA is free as long as both operands agree:
 // the V^T reads (ds_read_b64_tr_b16 on the row-major V rows) pick the keys in
@@ -26,14 +31,12 @@
 // one exchange for the column max (v_permlane32_swap, no LDS round trip).
 //
 // Softmax: log2 domain (scale times log2 e folded into one fma before exp2),
-// one running max per column per 64-key tile and lazy rescaling: the output is
-// only rescaled when a column's max grows by more than 2^8, which keeps exp2
-// arguments bounded and skips almost every rescale.  The output is normalised
-// by the sum of the bf16-rounded probabilities that the P.V product uses, so
-// the applied weights sum to one; that sum is itself two more MFMAs (an
-// all-ones A operand times P^T gives the column sums in every row).  The
-// returned lse comes from a lane-partial fp32 sum of the unrounded weights,
-// reduced once at the end.
+// one running max per column per unit and lazy rescaling: the max only moves
+// when a unit's max exceeds it by more than 2^8, which keeps exp2 arguments
+// bounded and skips almost every rescale.  The output is normalised by the
+// sum of the bf16-rounded probabilities that the P.V product uses, so the
+// applied weights sum to one; the returned lse comes from an fp32 sum of the
+// unrounded weights.  Both sums are lane-partial and reduced once at the end.
 //
 // Block ids enumerate the query blocks of all requests densely, in decreasing
 // order of the keys they see (computed in the kernel from the lengths), so the
@@ -51,18 +54,25 @@ typedef short shortx4_t __attribute__((ext_vector_type(4)));
 
 namespace pf {
 constexpr int kD = 128;
-constexpr int kKT = 64;                    // keys per tile
+constexpr int kKT = 64;                          // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kColsW = 32;                 // query columns per wave
-constexpr int kCols = kWaves * kColsW;     // query columns per block
-constexpr int kRow = kD * 2;               // bytes per K or V row in LDS
-constexpr int kHalf = kKT * kRow;          // the K rows of a stage, then its V rows
-constexpr int kStage = 2 * kHalf;
+constexpr int kColsW = 32;                       // query columns per wave
+constexpr int kCols = kWaves * kColsW;           // query columns per block
+constexpr int kRow = kD * 2;                     // bytes per K or V row in LDS
+constexpr int kTile = kKT * kRow;                // the K (or V) rows of one tile
 constexpr int kStages = 4;
-constexpr int kAhead = kStages - 1;        // tiles gathered ahead of the compute
-constexpr int kGathersPerTile = 16;        // vector memory instructions per wave per tile
+constexpr int kKBase = 0;                        // K tiles of the stages
+constexpr int kVBase = kStages * kTile;          // V tiles of the stages
+constexpr int kIdsBase = 2 * kStages * kTile;    // page-table ids: per wave, kIdSlots tiles
+constexpr int kIdSlots = 4;
+constexpr int kLds = kIdsBase + kWaves * kIdSlots * kKT * 4;
+constexpr int kAhead = kStages - 1;              // tiles gathered ahead of the compute
+constexpr int kIdsAhead = kStages + 1;           // tiles whose ids are copied ahead
+constexpr int kVmemPerTile = 5;                  // per wave and tile: 1 id copy + 4 gathers
 constexpr float kRescaleLog2 = 8.0f;
+static_assert(kIdsAhead - kAhead < kIdSlots && kIdsAhead == kIdSlots + 1 && kAhead >= 2,
+              "an id slot is refilled only after its gathers were issued (the prologue relies on these values)");
 }  // namespace pf
 
 MSGL_DEV floatx16_t mfma_32x32x16(const bf16x8_t &a, const bf16x8_t &b, const floatx16_t &c) {
@@ -82,15 +92,23 @@ MSGL_DEV float add_with_other_half(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane 4j+a names 4 consecutive 16-bit values; lane l receives value l%4 of
 // the lanes l/4, 4+l/4, 8+l/4 and 12+l/4.  When lanes 4j..4j+3 point at key
 // j's row at dims +0, +4, +8, +12, lane l therefore gets dim l of keys 0..3.
-MSGL_DEV uint2 lds_read_tr16(const char *p) {
+MSGL_DEV uint2 lds_read_tr16(uint32_t addr) {
     const shortx4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) shortx4_t *)(const_cast<char *>(p)));
+        (__attribute__((address_space(3))) shortx4_t *)(uintptr_t)addr);
     return __builtin_bit_cast(uint2, v);
 }
+
+MSGL_DEV bf16x8_t lds_read16(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) bf16x8_t *)(uintptr_t)addr;
+}
+
+MSGL_DEV int lds_read_i32(uint32_t addr) { return *(const __attribute__((address_space(3))) int *)(uintptr_t)addr; }
 
 // Row permutation code: chunk c of row r sits at chunk position c ^ code(r).
 // code is a bijection on r % 16, so 16 (or 8) consecutive rows read at one
@@ -101,44 +119,17 @@ MSGL_DEV int row_code(int r) {
     return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r ^ (r >> 3)) & 1) << 3);
 }
 
-// The 8 page-table ids of rows 8w..8w+7 of a tile (uniform per wave, scalar
-// loads, left unchecked until they are used).  Keys past the block's last one
-// read key 0's id: a real row whose scores the causal mask removes.
-typedef int TileIds __attribute__((ext_vector_type(8)));
-
-MSGL_DEV void load_ids(TileIds &ids, const __attribute__((address_space(4))) int32_t *pt, int key0, int nkeys) {
-    if (key0 + 8 <= nkeys) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ids[j] = pt[key0 + j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ids[j] = pt[key0 + j < nkeys ? key0 + j : 0];
-    }
+// Copies straight into LDS (global_load_lds_dword / _dwordx4): lane l's 4 or
+// 16 bytes land at LDS address lds + 4 l or + 16 l; lds is wave-uniform (M0).
+// Issued as inline assembly so that the compiler neither counts them nor holds
+// later LDS reads back for them: the kernel orders them itself (vmcnt waits
+// and barriers).
+MSGL_DEV void copy4_to_lds(const void *base, uint32_t lane_off, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(lds) : "memory");
 }
 
-// One gather of 4 bytes per lane straight into LDS (global_load_lds_dword):
-// lane l's bytes land at LDS address lds + 4 l (lds is wave-uniform, in M0);
-// the source is a wave-uniform row address plus a per-lane offset.  Issued as
-// inline assembly so that the compiler neither counts it nor holds later LDS
-// reads back for it: the kernel orders it itself (vmcnt + barrier).
-MSGL_DEV void gather_row_to_lds(const char *row, uint32_t lane_off, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(lane_off), "s"(row), "{m0}"(lds) : "memory");
-}
-
-// Gathers of one tile by one wave to LDS address `dst` (the stage + this
-// wave's first row): K rows, then V rows 8w..8w+7, one instruction per row.
-// Lane l fills bytes 4l..4l+3 of its row, i.e. chunk position l/4, so it
-// reads the chunk that the row permutation puts there.
-MSGL_DEV void issue_tile(uint32_t dst, TileIds ids, int wave, const char *kbase, int64_t v_minus_k,
-                         int64_t row_bytes, uint32_t lane4, uint32_t num_slots) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int s = (uint32_t)ids[j] < num_slots ? ids[j] : 0;  // a malformed id stays inside the pool
-        const char *krow = kbase + (int64_t)s * row_bytes;
-        const uint32_t off = lane4 ^ (row_code(8 * wave + j) << 4);
-        gather_row_to_lds(krow, off, dst + j * pf::kRow);
-        gather_row_to_lds(krow + v_minus_k, off, dst + pf::kHalf + j * pf::kRow);
-    }
+MSGL_DEV void copy16_to_lds(const void *src, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
 template <int N>
@@ -146,8 +137,8 @@ MSGL_DEV void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Workgroup barrier that orders LDS only (the gathers are ordered by the
-// explicit vmcnt waits before it).
+// Workgroup barrier that orders LDS only (the copies into LDS are ordered by
+// the explicit vmcnt waits before it).
 MSGL_DEV void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -262,7 +253,7 @@ template <int GQ>
 __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
     constexpr int BQ = pf::kCols / GQ;  // query tokens per block
     constexpr int S = pf::kStages;
-    __shared__ __attribute__((aligned(1024))) char smem[S * pf::kStage];
+    __shared__ __attribute__((aligned(1024))) char smem[pf::kLds];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -296,27 +287,53 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
     const int tok = valid ? tl : ntok - 1;
     const int pos = pos0 + tok;
 
-    // gather sources: page-table row, pools at this kv head, per-lane chunk offsets
-    const auto *pt = (const __attribute__((address_space(4))) int32_t *)(
-        a.page_table + (int64_t)a.table_idx[b] * a.row_stride);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)smem;
+    // page-table ids: each wave copies all 64 ids of a tile into its own slot
+    // (keys past the block's last one read key 0's id: a real row whose scores
+    // the causal mask removes)
+    const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
+    const uint32_t ids_wave = lds0 + pf::kIdsBase + wave * pf::kIdSlots * pf::kKT * 4;
+    auto copy_ids = [&](int t) __attribute__((always_inline)) {
+        const int key = t * pf::kKT + lane;
+        copy4_to_lds(pt, 4u * (uint32_t)(key < nkeys ? key : 0), ids_wave + (t % pf::kIdSlots) * pf::kKT * 4);
+    };
+    // gathers: per tile this wave fills rows 8w + 4i + l/16 (i = 0, 1) of K and
+    // V; lane l writes chunk position l%16 of its row, so it loads the chunk
+    // that the permutation puts there
     const uint32_t num_slots = (uint32_t)a.num_slots;
-    const int64_t row_bytes = (int64_t)G * pf::kD * 2;
-    const char *kbase = reinterpret_cast<const char *>(a.k_pool) + (int64_t)kvh * pf::kRow;
-    const int64_t v_minus_k = reinterpret_cast<const char *>(a.v_pool) - reinterpret_cast<const char *>(a.k_pool);
-    const uint32_t lane4 = 4 * lane;
-    const uint32_t lds_wave = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem +
-                              8 * wave * pf::kRow;  // this wave's first row of stage 0
-
-    // pipeline prologue: gathers of tiles 0..S-2, then Q, then the ids of tiles S-1 and S
-    TileIds ids_use, ids_next;
+    const uint32_t row_bytes = (uint32_t)G * pf::kRow;
+    const int grp = lane >> 4;
+    const char *kb[2], *vb[2];
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t) {
-        load_ids(ids_use, pt, t * pf::kKT + 8 * wave, nkeys);
-        issue_tile(lds_wave + t * pf::kStage, ids_use, wave, kbase, v_minus_k, row_bytes, lane4, num_slots);
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t off = (uint32_t)kvh * pf::kRow + (((lane & 15) ^ row_code(8 * wave + 4 * i + grp)) << 4);
+        kb[i] = reinterpret_cast<const char *>(a.k_pool) + off;
+        vb[i] = reinterpret_cast<const char *>(a.v_pool) + off;
     }
+    auto gather = [&](int t, int stage) __attribute__((always_inline)) {
+        const uint32_t ids = ids_wave + (t % pf::kIdSlots) * pf::kKT * 4 + (8 * wave + grp) * 4;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int s = lds_read_i32(ids + 16 * i);
+            s = (uint32_t)s < num_slots ? s : 0;  // a malformed id stays inside the pool
+            const uint32_t dst = lds0 + stage * pf::kTile + (8 * wave + 4 * i) * pf::kRow;
+            copy16_to_lds(kb[i] + (uint64_t)(uint32_t)s * row_bytes, dst + pf::kKBase);
+            copy16_to_lds(vb[i] + (uint64_t)(uint32_t)s * row_bytes, dst + pf::kVBase);
+        }
+    };
+
+    // pipeline prologue: ids of tiles 0..3, gathers of tiles 0..2 with the
+    // ids of tile 4 copied once the slot of tile 0 has been read, then Q
+#pragma unroll
+    for (int t = 0; t < pf::kIdSlots; ++t) copy_ids(t);
+    wait_vmcnt<pf::kIdSlots - pf::kAhead>();  // this wave's ids of tiles 0..2 (its own slots)
+    gather(0, 0);
+    copy_ids(pf::kIdSlots);
+#pragma unroll
+    for (int t = 1; t < pf::kAhead; ++t) gather(t, t);
     // Q^T operands: d-chunk dc holds dims 16*dc + 8*jj .. +7 of this column.
     // The empty asm below makes the compiler wait for them here, once; the
-    // gathers it cannot see are older, so they are complete then as well.
+    // copies it cannot see are older, so they are complete then as well.
     bf16x8_t qv[8];
     const bf16_t *qp = reinterpret_cast<const bf16_t *>(a.q) +
                        ((int64_t)(row0 + tok) * a.q_heads + hq) * pf::kD + 8 * jj;
@@ -324,39 +341,40 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
     for (int dc = 0; dc < 8; ++dc) qv[dc] = __builtin_bit_cast(bf16x8_t, ld16(qp + 16 * dc));
 #pragma unroll
     for (int dc = 0; dc < 8; ++dc) asm volatile("" ::"v"(qv[dc]));
-    load_ids(ids_use, pt, (S - 1) * pf::kKT + 8 * wave, nkeys);
-    load_ids(ids_next, pt, S * pf::kKT + 8 * wave, nkeys);
 
-    // LDS read offsets within a stage.  K (A of S^T): row (lane%32) [+32 for
-    // the second half], chunk 2*dc + jj.  V (A of O^T, transposing reads):
-    // lane L reads row 4*jj + (L/4)%4 [+8*qq, +32 for the second half] at
-    // dims 32*db + 16*((L/16)%2) + 4*(L%4), i.e. chunk 4*db + vch, byte 8*(L%2).
-    const int kx = row_code(lane & 15) ^ jj;
-    const int krow = (lane & 31) * pf::kRow;
-    const int vrow = 4 * jj + ((lane >> 2) & 3);
-    const int vch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    const int vx0 = vrow * pf::kRow + ((vch ^ row_code(vrow)) << 4) + (lane & 1) * 8;      // qq even
-    const int vx1 = vrow * pf::kRow + ((vch ^ row_code(vrow + 8)) << 4) + (lane & 1) * 8;  // qq odd
+    // LDS read addresses, per lane, of stage 0's first half (stages and halves
+    // are immediate offsets).  K (A of S^T): row lane%32, chunk 2*dc + jj.
+    // V (A of O^T, transposing reads): lane L reads row 4*jj + (L/4)%4 [+8*qq]
+    // at dims 32*db + 16*((L/16)%2) + 4*(L%4), i.e. chunk 4*db + vch, byte 8*(L%2).
+    uint32_t kaddr[8], vaddr[4][2];
+    {
+        const int kx = row_code(lane & 15) ^ jj;
+        const int vrow = 4 * jj + ((lane >> 2) & 3);
+        const int vch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int dc = 0; dc < 8; ++dc) kaddr[dc] = lds0 + pf::kKBase + (lane & 31) * pf::kRow + (((2 * dc) ^ kx) << 4);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int par = 0; par < 2; ++par)
+                vaddr[db][par] = lds0 + pf::kVBase + vrow * pf::kRow +
+                                 (((4 * db + vch) ^ row_code(vrow + 8 * par)) << 4) + (lane & 1) * 8;
+    }
 
-    // The key sequence is processed in units of 32 keys (half a tile).  Unit
-    // u's scores are computed two units ahead of its P.V and its softmax one
-    // unit ahead, so that every unit's MFMAs (scores of u+2, P.V of u) and its
-    // VALU work (softmax of u+1) are independent and can overlap.
     floatx16_t acc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = floatx16_t{};
- float ls = 0.0f;                  // this lane's share of the running sum of the bf16-rounded weights
     float m;                          // running column max (log2 units; may lag by < 2^8)
     float lt = 0.0f;                  // this lane's share of the running sum of the weights (for lse)
+    float ls = 0.0f;                  // ... and of the bf16-rounded weights (for normalising)
     floatx16_t sc;                    // raw scores of the unit whose softmax is next
     bf16x8_t pb[2];                   // weights of the unit whose P.V is next
 
-    auto scores = [&](int u) __attribute__((always_inline)) {
-        const char *kr = smem + ((u >> 1) % S) * pf::kStage + (u & 1) * 32 * pf::kRow + krow;
+    auto scores = [&](int stage, int half) __attribute__((always_inline)) {
         floatx16_t s = floatx16_t{};
 #pragma unroll
         for (int dc = 0; dc < 8; ++dc)
-            s = mfma_32x32x16(*reinterpret_cast<const bf16x8_t *>(kr + (((2 * dc) ^ kx) << 4)), qv[dc], s);
+            s = mfma_32x32x16(lds_read16(kaddr[dc] + stage * pf::kTile + half * 32 * pf::kRow), qv[dc], s);
         return s;
     };
     auto mask = [&](floatx16_t &s, int u) __attribute__((always_inline)) {
@@ -369,105 +387,118 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
         }
     };
     auto column_max = [&](const floatx16_t &s) __attribute__((always_inline)) {
-        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        float mx = fmaxf(s[0], fmaxf(s[1], s[2]));
 #pragma unroll
-        for (int e = 4; e < 16; e += 4) mx = fmaxf(mx, fmaxf(fmaxf(s[e], s[e + 1]), fmaxf(s[e + 2], s[e + 3])));
+        for (int e = 3; e < 15; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+        mx = fmaxf(mx, s[15]);
         return max_with_other_half(mx) * a.scale_log2;  // raw scores: the scale is positive
     };
-    auto weights = [&](const floatx16_t &s, bf16x8_t (&out)[2]) __attribute__((always_inline)) {
-        const float nmu = -m;
+    // weights exp2(s * scale - mu), rounded pairs for P.V, and their two sums
+    auto weights = [&](const floatx16_t &s, float mu, bf16x8_t (&out)[2], float &sum, float &sum_rounded)
+        __attribute__((always_inline)) {
         uint32_t pw[8];
+        sum = 0.0f;
+        sum_rounded = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
-            const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, nmu));
-            const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, nmu));
+            const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, -mu));
+            const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, -mu));
             pw[e >> 1] = pack_bf16x2(p0, p1);
-            lt += p0 + p1;
-            ls = dot2_bf16(pw[e >> 1], 0x3f803f80u, ls);  // the rounded pair, as P.V will use it
+            sum += p0 + p1;
+            sum_rounded = dot2_bf16(pw[e >> 1], 0x3f803f80u, sum_rounded);  // the pair as P.V will use it
         }
         out[0] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
         out[1] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
     };
-    auto pv = [&](int u) __attribute__((always_inline)) {
-        const char *vs = smem + ((u >> 1) % S) * pf::kStage + pf::kHalf + (u & 1) * 32 * pf::kRow;
+    auto pv = [&](int stage, int half) __attribute__((always_inline)) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
             uint2 av[4];
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq)
-                av[qq] = lds_read_tr16(vs + 8 * qq * pf::kRow + ((qq & 1 ? vx1 : vx0) ^ (db << 6)));
+                av[qq] = lds_read_tr16(vaddr[db][qq & 1] + stage * pf::kTile + half * 32 * pf::kRow +
+                                       8 * qq * pf::kRow);
             acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(av[0].x, av[0].y, av[1].x, av[1].y)),
                                     pb[0], acc[db]);
             acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(av[2].x, av[2].y, av[3].x, av[3].y)),
                                     pb[1], acc[db]);
         }
     };
-    // One unit: P.V of unit u, the softmax of unit u+1 (whose scores are in
-    // sc) and, if there is one, the scores of unit u+2.
-    auto unit = [&](int u, bool has_scores, bool has_softmax) __attribute__((always_inline)) {
+    // One unit: P.V of unit u (tile stage `stage`, half u%2), the softmax of
+    // unit u+1 (its scores are in sc) and, if there is one, the scores of
+    // unit u+2 (the same half of the next tile, stage `next`).
+    auto unit = [&](int u, int stage, int next, bool has_scores, bool has_softmax) __attribute__((always_inline)) {
+        const int half = u & 1;
         if (has_softmax) mask(sc, u + 1);
         floatx16_t s_new;
-        if (has_scores) s_new = scores(u + 2);
-        pv(u);
-        float alpha = 1.0f;
+        if (has_scores) s_new = scores(next, half);
+        pv(stage, half);
+        float mn = m, lt_u = 0.0f, ls_u = 0.0f;
         bf16x8_t pb_new[2];
         if (has_softmax) {
             const float mx = column_max(sc);
-            const float mn = mx > m + pf::kRescaleLog2 ? mx : m;  // lazy: move the max only by more than 2^8
-            alpha = fast_exp2(m - mn);
-            m = mn;
-            lt *= alpha;
-            ls *= alpha;
-            weights(sc, pb_new);
+            mn = mx > m + pf::kRescaleLog2 ? mx : m;  // lazy: move the max only by more than 2^8
+            weights(sc, mn, pb_new, lt_u, ls_u);
             // keep the weights in this block (the compiler would otherwise sink
             // them past the rescale branch, away from the MFMAs they overlap)
-            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt), "v"(ls));
+            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u), "v"(ls_u));
         }
         if (has_scores && has_softmax) interleave_unit<0, 16>();
-        if (has_softmax && __any(alpha != 1.0f)) {  // rare: rescale what P.V of units <= u accumulated
+        if (has_softmax && __any(mn != m)) {  // rare: rescale what units <= u accumulated
+            const float alpha = fast_exp2(m - mn);
+            lt *= alpha;
+            ls *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
         }
         if (has_softmax) {
+            m = mn;
+            lt += lt_u;
+            ls += ls_u;
             pb[0] = pb_new[0];
             pb[1] = pb_new[1];
         }
         if (has_scores) sc = s_new;
     };
+    // Tile t < ntiles-1 (its stage is t % S): refill the stage of tile t-1
+    // with tile t+S-1, copy the ids of tile t+S+1, then units 2t and 2t+1.
+    auto tile = [&](int t, int stage) __attribute__((always_inline)) {
+        // this wave's copies of tile t+1 (and of the ids of tile t+S-1) are
+        // done, the later ones may still be in flight; after the barrier
+        // everyone's are, and every wave has finished reading tile t-1's stage
+        wait_vmcnt<(S - 3) * pf::kVmemPerTile>();
+        lds_barrier();
+        copy_ids(t + pf::kIdsAhead);
+        gather(t + pf::kAhead, (stage + pf::kAhead) % S);  // past the end: harmless reloads
+        const int next = (stage + 1) % S;
+        unit(2 * t, stage, next, true, true);
+        unit(2 * t + 1, stage, next, true, true);
+    };
 
     // scores and weights of unit 0, scores of unit 1 (tile 0)
-    wait_vmcnt<(S - 2) * pf::kGathersPerTile>();
     lds_barrier();
     {
-        floatx16_t s0 = scores(0);
-        sc = scores(1);
+        floatx16_t s0 = scores(0, 0);
+        sc = scores(0, 1);
         mask(s0, 0);
         m = column_max(s0);  // key 0 is visible to every column: finite
-        weights(s0, pb);
+        weights(s0, m, pb, lt, ls);
     }
-    for (int t = 0; t + 1 < ntiles; ++t) {
-        // this wave's gathers of tile t+1 are done (the later tiles' may still
-        // be in flight); after the barrier everyone's are, and every wave has
-        // finished reading tile t-1's stage, which is refilled with tile t+S-1
-        wait_vmcnt<(S - 3) * pf::kGathersPerTile>();
-        lds_barrier();
-        {
-            TileIds ids_new;
-            load_ids(ids_new, pt, (t + S + 1) * pf::kKT + 8 * wave, nkeys);
-            issue_tile(lds_wave + ((t + S - 1) % S) * pf::kStage, ids_use, wave, kbase, v_minus_k, row_bytes,
-                       lane4, num_slots);  // past the end: harmless reloads
-            ids_use = ids_next;
-            ids_next = ids_new;
-        }
-        unit(2 * t, true, true);
-        unit(2 * t + 1, true, true);
+    int t = 0;
+    for (; t + S <= ntiles - 1; t += S) {
+        tile(t, 0);
+        tile(t + 1, 1);
+        tile(t + 2, 2);
+        tile(t + 3, 3);
     }
-    // the last tile: it is resident since the previous iteration (or the prologue)
-    unit(2 * ntiles - 2, false, true);
-    unit(2 * ntiles - 1, false, false);
-    // the gathers issued past the last tile must land before the block's LDS is released
+    for (; t < ntiles - 1; ++t) tile(t, t % S);
+    // the last tile: resident since the previous iteration (or the prologue)
+    const int last = (ntiles - 1) % S;
+    unit(2 * ntiles - 2, last, 0, false, true);
+    unit(2 * ntiles - 1, last, 0, false, false);
+    // the copies issued past the last tile must land before the block's LDS is released
     wait_vmcnt<0>();
 
     lt = add_with_other_half(lt);
