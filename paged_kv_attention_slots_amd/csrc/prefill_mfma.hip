@@ -13,8 +13,8 @@
 // destination + 16 l, so one instruction fills 4 rows), three tiles ahead of
 // the compute.  The page-table ids of a tile are copied into LDS the same way
 // two tiles before its gathers.  Every iteration issues the same five vector
-// memory instructions per wave, so one vmcnt wait plus one barrier per tile
-// is exact.  The main loop is unrolled over the 4 stages so that every LDS
+// memory instructions per wave (fewer near the end: no gathers past the last
+// tile), so one vmcnt wait plus one barrier per tile is exact.  The main loop is unrolled over the 4 stages so that every LDS
 // read address is a per-lane register plus an immediate.
 //
 // Keys are processed in units of 32 (half a tile).  For unit u a wave
@@ -69,8 +69,10 @@ constexpr int kIdSlots = 4;
 constexpr int kLds = kIdsBase + kWaves * kIdSlots * kKT * 4;
 constexpr int kAhead = kStages - 1;              // tiles gathered ahead of the compute
 constexpr int kIdsAhead = kStages + 1;           // tiles whose ids are copied ahead
-constexpr int kVmemPerTile = 5;                  // per wave and tile: 1 id copy + 4 gathers
+constexpr int kIdsPerTile = 1;                   // per wave and tile: 1 id copy ...
+constexpr int kVmemPerTile = kIdsPerTile + 4;    // ... and 4 gathers (none past the last tile)
 constexpr float kRescaleLog2 = 8.0f;
+constexpr int kMaxBatch = 1024;                  // requests per call on the MFMA path
 static_assert(kIdsAhead - kAhead < kIdSlots && kIdsAhead == kIdSlots + 1 && kAhead >= 2,
               "an id slot is refilled only after its gathers were issued (the prologue relies on these values)");
 }  // namespace pf
@@ -123,13 +125,21 @@ MSGL_DEV int row_code(int r) {
 // 16 bytes land at LDS address lds + 4 l or + 16 l; lds is wave-uniform (M0).
 // Issued as inline assembly so that the compiler neither counts them nor holds
 // later LDS reads back for them: the kernel orders them itself (vmcnt waits
-// and barriers).
+// and barriers).  The compiler does not see the memory instruction inside, so
+// it cannot insert the wait states the hardware needs between a VALU write of
+// a scalar register (a readfirstlane of the base, or M0) or of an address
+// register and this read of it: the s_nop 4 (5 wait states) covers them.
 MSGL_DEV void copy4_to_lds(const void *base, uint32_t lane_off, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(lds) : "memory");
+    // the base must live in scalar registers: make its uniformity explicit
+    const uint64_t b = (uint64_t)base;
+    const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(lane_off), "s"((const void *)ub), "{m0}"(lds)
+                 : "memory");
 }
 
 MSGL_DEV void copy16_to_lds(const void *src, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
 template <int N>
@@ -146,11 +156,18 @@ MSGL_DEV void lds_barrier() {
 }
 
 // Instruction order hint for one unit's main block: the first LDS reads up
-// front, then one MFMA, a few VALU instructions and the next LDS read in
+// front, then two MFMAs, about ten VALU instructions and the next LDS reads in
 // turn, so that the matrix core and the vector ALU work side by side instead
-// of in phases, and every MFMA finds its LDS operand already loaded.
+// of in phases, and every MFMA finds its LDS operand already loaded (the
+// other orders are kept for tuning).
 #ifndef MSGL_PREFILL_SCHED
-#define MSGL_PREFILL_SCHED 2
+#define MSGL_PREFILL_SCHED 4
+#endif
+#ifndef MSGL_PF_M
+#define MSGL_PF_M 2    // MFMAs per group
+#define MSGL_PF_V 10   // VALU instructions per group
+#define MSGL_PF_D 3    // LDS reads per group
+#define MSGL_PF_D0 8   // LDS reads ahead of the first group
 #endif
 template <int I, int N>
 MSGL_DEV void interleave_unit() {
@@ -159,8 +176,14 @@ MSGL_DEV void interleave_unit() {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);              // VALU
         interleave_unit<I + 1, N>();
-    } else if constexpr (MSGL_PREFILL_SCHED >= 2 && I < N) {
-        constexpr int kValu = MSGL_PREFILL_SCHED == 2 ? 6 : 4;
+    } else if constexpr (MSGL_PREFILL_SCHED == 4 && I * MSGL_PF_M < N) {
+        if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, MSGL_PF_D0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MSGL_PF_M, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, MSGL_PF_V, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, MSGL_PF_D, 0);
+        interleave_unit<I + 1, N>();
+    } else if constexpr (MSGL_PREFILL_SCHED >= 2 && MSGL_PREFILL_SCHED != 4 && I < N) {
+        constexpr int kValu = MSGL_PREFILL_SCHED == 2 ? 6 : MSGL_PREFILL_SCHED == 3 ? 4 : 5;
         if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
@@ -171,9 +194,12 @@ MSGL_DEV void interleave_unit() {
 
 // Sum over the 64 lanes of a wave (every lane gets the total).
 MSGL_DEV int wave_sum(int v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+    v += __builtin_amdgcn_update_dpp(0, v, kDppXor1, 0xF, 0xF, false);       // pairs
+    v += __builtin_amdgcn_update_dpp(0, v, kDppXor2, 0xF, 0xF, false);       // quads
+    v += __builtin_amdgcn_update_dpp(0, v, kDppHalfMirror, 0xF, 0xF, false); // 8 lanes
+    v += __builtin_amdgcn_update_dpp(0, v, kDppMirror, 0xF, 0xF, false);     // 16-lane rows
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+           __builtin_amdgcn_readlane(v, 48);
 }
 
 // The query blocks of all requests, in decreasing order of the number of key
@@ -187,34 +213,46 @@ struct BlockItem {
     int qb;
 };
 
-template <int BQ>
+// NB = number of requests each lane keeps in registers (batch <= 64 NB); the
+// lengths are read once.
+template <int BQ, int NB>
 MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
-    // new and cached tokens of request b (no blocks when the request is malformed)
-    auto extend = [&](int b, int &E, int &C) __attribute__((always_inline)) {
-        const int L = (int)min((int64_t)a.seq_lens[b], a.row_stride);
-        C = a.cached_lens[b];
-        E = C < 0 ? 0 : L - C;
-    };
+    // new and cached tokens of the lane's requests (no blocks when a request is malformed)
+    int E[NB], C[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        const int b = lane + 64 * k;
+        E[k] = 0;
+        C[k] = 0;
+        if (b < a.batch) {
+            const int L = (int)min((int64_t)a.seq_lens[b], a.row_stride);
+            C[k] = a.cached_lens[b];
+            E[k] = C[k] < 0 ? 0 : L - C[k];
+        }
+    }
     // first query block of a request with more than x key tiles (nb if none)
-    auto first_above = [&](int E, int C, int x) __attribute__((always_inline)) {
-        const int y = pf::kKT * x - C;  // needs min((q+1) BQ, E) > y
-        const int nb = (E + BQ - 1) / BQ;
-        return E > y ? (y < 0 ? 0 : y / BQ) : nb;
+    auto first_above = [&](int e, int c, int x) __attribute__((always_inline)) {
+        const int y = pf::kKT * x - c;  // needs min((q+1) BQ, E) > y
+        const int nb = (e + BQ - 1) / BQ;
+        return e > y ? (y < 0 ? 0 : y / BQ) : nb;
     };
     // number of query blocks with more than x key tiles
     auto count_above = [&](int x) __attribute__((always_inline)) {
         int n = 0;
-        for (int b = lane; b < a.batch; b += 64) {
-            int E, C;
-            extend(b, E, C);
-            if (E > 0) n += (E + BQ - 1) / BQ - first_above(E, C, x);
-        }
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+            if (E[k] > 0) n += (E[k] + BQ - 1) / BQ - first_above(E[k], C[k], x);
         return wave_sum(n);
     };
-    const int xmax = (int)min((a.row_stride + pf::kKT - 1) / pf::kKT, (int64_t)1 << 24);
     if (count_above(0) <= r) return {-1, 0};
     // tile count x of entry r: the largest x with more than r blocks of >= x tiles
-    int lo = 1, hi = xmax + 1;
+    int most = 0;  // the most key tiles any block sees
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+        if (E[k] > 0) most = max(most, (C[k] + E[k] + pf::kKT - 1) / pf::kKT);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) most = max(most, __shfl_xor(most, off));
+    int lo = 1, hi = most + 1;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (count_above(mid - 1) > r) lo = mid;
@@ -222,16 +260,12 @@ MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
     }
     // the k-th block with exactly lo tiles, in request order
     int k = r - count_above(lo);
-    for (int base = 0; base < a.batch; base += 64) {
-        const int b = base + lane;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
         int c = 0, q0 = 0;
-        if (b < a.batch) {
-            int E, C;
-            extend(b, E, C);
-            if (E > 0) {
-                q0 = first_above(E, C, lo - 1);
-                c = first_above(E, C, lo) - q0;
-            }
+        if (E[j] > 0) {
+            q0 = first_above(E[j], C[j], lo - 1);
+            c = first_above(E[j], C[j], lo) - q0;
         }
         int incl = c;
 #pragma unroll
@@ -242,7 +276,7 @@ MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
         const unsigned long long hit = __ballot(k >= incl - c && k < incl);
         if (hit != 0) {
             const int src = __builtin_ctzll(hit);
-            return {__shfl(b, src), __shfl(q0 + k - (incl - c), src)};
+            return {__shfl(lane + 64 * j, src), __shfl(q0 + k - (incl - c), src)};
         }
         k -= __shfl(incl, 63);
     }
@@ -263,7 +297,9 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
 
     // block id = list entry * G + kv head: the query blocks longest first, no gaps
     const int kvh = blockIdx.x % G;
-    const BlockItem item = sorted_block<BQ>(a, blockIdx.x / G, lane);
+    const BlockItem item = a.batch <= 64    ? sorted_block<BQ, 1>(a, blockIdx.x / G, lane)
+                           : a.batch <= 256 ? sorted_block<BQ, 4>(a, blockIdx.x / G, lane)
+                                            : sorted_block<BQ, pf::kMaxBatch / 64>(a, blockIdx.x / G, lane);
     const int b = __builtin_amdgcn_readfirstlane(item.b);
     const int qb = __builtin_amdgcn_readfirstlane(item.qb);
     if (b < 0) return;  // past the last query block: uniform over the block, before any barrier
@@ -330,7 +366,8 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
     gather(0, 0);
     copy_ids(pf::kIdSlots);
 #pragma unroll
-    for (int t = 1; t < pf::kAhead; ++t) gather(t, t);
+    for (int t = 1; t < pf::kAhead; ++t)
+        if (t < ntiles) gather(t, t);
     // Q^T operands: d-chunk dc holds dims 16*dc + 8*jj .. +7 of this column.
     // The empty asm below makes the compiler wait for them here, once; the
     // copies it cannot see are older, so they are complete then as well.
@@ -468,10 +505,11 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
         // this wave's copies of tile t+1 (and of the ids of tile t+S-1) are
         // done, the later ones may still be in flight; after the barrier
         // everyone's are, and every wave has finished reading tile t-1's stage
-        wait_vmcnt<(S - 3) * pf::kVmemPerTile>();
+        if (t + S - 2 < ntiles) wait_vmcnt<(S - 3) * pf::kVmemPerTile>();
+        else wait_vmcnt<(S - 3) * pf::kIdsPerTile>();  // some later tiles had no gathers: count only the id copies
         lds_barrier();
-        copy_ids(t + pf::kIdsAhead);
-        gather(t + pf::kAhead, (stage + pf::kAhead) % S);  // past the end: harmless reloads
+        copy_ids(t + pf::kIdsAhead);  // past the end: a harmless copy of key 0's id
+        if (t + pf::kAhead < ntiles) gather(t + pf::kAhead, (stage + pf::kAhead) % S);
         const int next = (stage + 1) % S;
         unit(2 * t, stage, next, true, true);
         unit(2 * t + 1, stage, next, true, true);
@@ -498,7 +536,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
     const int last = (ntiles - 1) % S;
     unit(2 * ntiles - 2, last, 0, false, true);
     unit(2 * ntiles - 1, last, 0, false, false);
-    // the copies issued past the last tile must land before the block's LDS is released
+    // the id copies issued past the last tile must land before the block's LDS is released
     wait_vmcnt<0>();
 
     lt = add_with_other_half(lt);
@@ -537,7 +575,7 @@ hipError_t run_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, DType dtype, int head_dim, hipStream_t stream) {
-    if (dtype == kBF16 && head_dim == pf::kD) {
+    if (dtype == kBF16 && head_dim == pf::kD && a.batch <= pf::kMaxBatch) {
         switch (a.q_heads / a.kv_heads) {
             case 1: return run_prefill_mfma<1>(a, stream);
             case 2: return run_prefill_mfma<2>(a, stream);
