@@ -133,7 +133,7 @@ def msgl_decode_workspace_bytes(batch: int, q_heads: int, head_dim: int, max_seq
 
 def decode_workspace(batch: int, q_heads: int, head_dim: int, max_seq_len: int, chunk: int = 0,
                      device="cuda") -> torch.Tensor:
-    """A zero-filled workspace (its control block must start at zero)."""
+    """A workspace for msgl_decode_attn (zero-filled here; its contents need no initialisation)."""
     n = msgl_decode_workspace_bytes(batch, q_heads, head_dim, max_seq_len, chunk)
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
