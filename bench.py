@@ -414,12 +414,32 @@ def main() -> int:
     torch.cuda.synchronize()
     attn_ms = ka.elapsed_time(kb) / args.kernel_iters
 
+    # prefill attention on its own: back-to-back launches (the step's leg above
+    # also holds store_kv and starts with the pools just swept by the decode)
+    log(f"timing {args.kernel_iters} prefill-attention launches")
+
+    def prefill_attn_only():
+        _lib.msgl_prefill_attn(out3, lse3, w3.q, w3.k_pool, w3.v_pool, w3.page_table, w3.table_idx,
+                               w3.seq_lens, w3.cached_lens, w3.cu_q, max_ext3, page_size=w3.page_size,
+                               sm_scale=w3.sm_scale, stream=stream)
+
+    for _ in range(3):
+        prefill_attn_only()
+    torch.cuda.synchronize()
+    ka.record(stream)
+    for _ in range(args.kernel_iters):
+        prefill_attn_only()
+    kb.record(stream)
+    torch.cuda.synchronize()
+    pattn_ms = ka.elapsed_time(kb) / args.kernel_iters
+
     dbytes = decode_bytes(w4)
     sbytes = store_bytes(w4)
     flops3 = prefill_flops(w3)
     value = (dbytes + sbytes) / (dec_ms * 1e-3) / 1e9
     attn_gbs = dbytes / (attn_ms * 1e-3) / 1e9
     prefill_tflops = flops3 / (pre_ms * 1e-3) / 1e12
+    pattn_tflops = flops3 / (pattn_ms * 1e-3) / 1e12
     req_tok_s = w4.bs / (dec_ms * 1e-3)
 
     cpu = None
@@ -479,6 +499,9 @@ def main() -> int:
         "req_tokens_per_s": round(req_tok_s, 1),
         "prefill_tflops": round(prefill_tflops, 2),
         "prefill_frac_of_bf16_peak": round(prefill_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+        "prefill_attn_ms": round(pattn_ms, 4),
+        "prefill_attn_tflops": round(pattn_tflops, 2),
+        "prefill_attn_frac_of_bf16_peak": round(pattn_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode attention (split + merge), eager, bs 256",
