@@ -305,7 +305,33 @@ def mixed(iters: int) -> int:
     return 0
 
 
+def prefill_profile(iters: int) -> int:
+    """Only the ragged prefill attention (8 requests, Qwen3-0.6B heads),
+    launched back to back: the command the prefill counter profiles run."""
+    import torch
+    from paged_kv_attention_slots_amd import _lib, workloads as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.ragged_prefill(device=dev)
+    out = torch.empty_like(w.q)
+    lse = torch.empty(w.num_tokens, w.q_heads, dtype=torch.float32, device=dev)
+    me = int((w.seq_lens - w.cached_lens).max())
+    stream = torch.cuda.Stream(device=dev)
+
+    def call():
+        _lib.msgl_prefill_attn(out, lse, w.q, w.k_pool, w.v_pool, w.page_table, w.table_idx, w.seq_lens,
+                               w.cached_lens, w.cu_q, me, page_size=w.page_size, sm_scale=w.sm_scale,
+                               stream=stream)
+
+    ms = _time_stream(call, stream, iters)
+    print(json.dumps({"prefill_profile": "ragged prefill 8 req", "launches": iters + 3, "ms": round(ms, 4),
+                      "tflops": round(prefill_flops(w) / (ms * 1e-3) / 1e12, 2)}), flush=True)
+    return 0
+
+
 def main() -> int:
+    if len(sys.argv) > 1 and sys.argv[1] == "--prefill-profile":
+        return prefill_profile(int(sys.argv[2]) if len(sys.argv) > 2 else 20)
     if len(sys.argv) > 1 and sys.argv[1] == "--mixed":
         return mixed(int(sys.argv[2]) if len(sys.argv) > 2 else 5)
     if len(sys.argv) > 1 and sys.argv[1] == "--sweep":
