@@ -418,17 +418,21 @@ def qwen3_06b_decode(seed: int = 1002, device="cpu", bs: int = 64, lo: int = 512
 def ragged_prefill(seed: int = 1003, device="cpu", n_req: int = 8, e_lo: int = 128, e_hi: int = 2048,
                    c_lo: int = 0, c_hi: int = 1024, num_slots: int = 1 << 15,
                    q_std: Optional[float] = None, dtype: torch.dtype = torch.bfloat16,
-                   heads=QWEN3_06B) -> Workload:
+                   heads=QWEN3_06B, page_size: int = 1) -> Workload:
     """Ragged causal prefill/extend (16q/8kv, d128, bf16): 8 requests, extend
     lengths U[128, 2048] on a resident cached prefix U[0, 1024]; shuffled free
-    list, each request's prefix slots first, then its new tokens."""
+    list, each request's prefix slots first, then its new tokens (at page size
+    > 1: shuffled free pages, each request's tokens in page order)."""
     rng = np.random.default_rng(seed)
     ext = rng.integers(e_lo, e_hi, size=n_req, endpoint=True)
     cac = rng.integers(c_lo, c_hi, size=n_req, endpoint=True)
     lens = ext + cac
-    free = rng.permutation(num_slots)
-    rows = rows_from_free_slots(free, lens, new_after_history=False)
-    return build_workload("ragged-prefill", "prefill", dtype, **heads, page_size=1,
+    if page_size == 1:
+        free = rng.permutation(num_slots)
+        rows = rows_from_free_slots(free, lens, new_after_history=False)
+    else:
+        rows = rows_from_free_pages(rng.permutation(num_slots // page_size), lens, page_size)
+    return build_workload("ragged-prefill", "prefill", dtype, **heads, page_size=page_size,
                           num_slots=num_slots, max_running_req=n_req, max_seq_len=c_hi + e_hi,
                           rows=rows, seq_lens=lens, cached_lens=cac, seed=seed, kv_std=1.0,
                           q_std=q_std if q_std is not None else 1.0 / math.sqrt(128), device=device)

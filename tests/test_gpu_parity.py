@@ -129,6 +129,40 @@ def test_ragged_prefill_long_prefix(oracle_mod, runner, wl):
     _full_check(oracle_mod, runner, w, rowsum_reqs=[1])
 
 
+@pytest.mark.parametrize("n_req", [100, 300])
+def test_ragged_prefill_many_requests(oracle_mod, runner, wl, n_req):
+    # more than 64 and more than 256 requests: the block enumeration keeps 4
+    # or 16 requests per lane; short extends, some of one token
+    w = wl.ragged_prefill(device="cuda", n_req=n_req, e_lo=1, e_hi=40, c_lo=0, c_hi=100,
+                          num_slots=1 << 16, seed=50 + n_req)
+    _full_check(oracle_mod, runner, w, rowsum_reqs=[0, n_req - 1])
+
+
+def test_ragged_prefill_page16(oracle_mod, runner, wl):
+    # page size 16: the page table holds token-level slots of shuffled pages
+    w = wl.ragged_prefill(device="cuda", n_req=4, e_lo=1, e_hi=300, c_lo=0, c_hi=400, num_slots=1 << 13,
+                          seed=47, page_size=16)
+    _full_check(oracle_mod, runner, w, rowsum_reqs=[0, 3])
+
+
+def test_ragged_prefill_beyond_mfma_batch(oracle_mod, runner, wl):
+    # more requests than the matrix-core kernel takes (1024): the vector-ALU
+    # kernel serves the call; sampled rows against the oracle
+    w = wl.ragged_prefill(device="cuda", n_req=1030, e_lo=1, e_hi=6, c_lo=0, c_hi=60, num_slots=1 << 17,
+                          seed=48)
+    res = runner.run_step(w)
+    torch.cuda.synchronize()
+    kp, vp = oracle_mod.store_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.out_loc)
+    assert store_mismatch(w, res.k_pool, res.v_pool, kp, vp) == 0
+    rows = sample_rows(w, 256)
+    out_ref, lse_ref = oracle_rows(oracle_mod, w, kp, vp, rows)
+    idx = torch.from_numpy(rows).cuda()
+    err = max_abs(res.out[idx], out_ref)
+    say(f"[parity] prefill with {w.bs} requests, sampled {len(rows)} rows: max-abs {err:.3e}")
+    assert err <= tol(w), err
+    assert max_abs(res.lse[idx], lse_ref) < 1e-3
+
+
 def test_ragged_prefill_v_ones_exact(runner, wl):
     w = wl.ragged_prefill(device="cuda", n_req=3, e_lo=30, e_hi=300, c_lo=0, c_hi=200, num_slots=1 << 11,
                           seed=46)
