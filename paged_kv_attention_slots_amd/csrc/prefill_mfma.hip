@@ -3,20 +3,32 @@
 // New token i of request b sits at position p = cached_len + i and attends
 // keys 0..p of its page-table row: a causal mask offset by the cached prefix.
 //
-// Block = one kv head x 256 query "columns", one block per CU.  A column is a
+// A block covers one kv head and a set of query "columns".  A column is a
 // (token, q head) pair of the q heads that share the kv head (token-major), so
-// every gathered K/V tile serves the whole group; each of the 8 waves owns 32
-// columns.  Keys stream through a ring of 4 LDS stages of 64-key tiles (K rows
-// and V rows of 256 bytes, their 16-byte chunks permuted per row so that the
-// column-wise reads below hit every bank once).  The gathers go straight from
-// the pools into LDS (global_load_lds_dwordx4: lane l's 16 bytes land at the
-// destination + 16 l, so one instruction fills 4 rows), three tiles ahead of
-// the compute.  The page-table ids of a tile are copied into LDS the same way
-// two tiles before its gathers.  Every iteration issues the same five vector
-// memory instructions per wave (fewer near the end: no gathers past the last
-// tile), so one vmcnt wait plus one barrier per tile is exact.  The main loop is unrolled over the 4 stages so that every LDS
-// read address is a per-lane register plus an immediate.
+// every gathered K/V tile serves the whole group; each wave owns 32 columns.
+// Keys stream through LDS in 64-key tiles (K rows and V rows of 256 bytes,
+// their 16-byte chunks permuted per row so that the column-wise reads below
+// hit every bank once).  The gathers go straight from the pools into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the destination + 16 l,
+// so one instruction fills 4 rows), and so do the page-table ids of a tile
+// (global_load_lds_dword) ahead of its gathers.  Two layouts:
 //
+//  - prefill_mfma_kernel: 4 waves (128 columns), K and V rings of two tiles,
+//    68 KB of LDS, so two blocks share a CU and one computes while the other
+//    starts up or waits.  At each tile the wave waits for all its copies (K of
+//    the next tile, V of this one, issued one tile earlier) and a barrier
+//    makes everyone's visible.
+//  - prefill_mfma_long_kernel: 8 waves (256 columns), one ring of 4 tiles,
+//    gathers three tiles ahead, one block per CU.  Every iteration issues the
+//    same five vector memory instructions per wave (fewer near the end: no
+//    gathers past the last tile), so one vmcnt wait that leaves the last
+//    tile's copies in flight plus one barrier per tile is exact.  It serves
+//    long uniform chunks (2048 or more new tokens per request on average),
+//    where its deeper ring beats the other layout's hiding of block starts.
+//
+// Both unroll the main loop over the ring's stages so that every LDS read
+// address is a per-lane register plus an immediate.
+
 // Keys are processed in units of 32 (half a tile).  For unit u a wave
 // computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims
 // from LDS, B = Q^T held in registers, 8 steps over head_dim 128) two units
@@ -52,30 +64,46 @@ namespace msgl {
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
 typedef short shortx4_t __attribute__((ext_vector_type(4)));
 
-namespace pf {
+namespace pf {  // shared by both layouts
 constexpr int kD = 128;
 constexpr int kKT = 64;                          // keys per tile
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kColsW = 32;                       // query columns per wave
-constexpr int kCols = kWaves * kColsW;           // query columns per block
 constexpr int kRow = kD * 2;                     // bytes per K or V row in LDS
 constexpr int kTile = kKT * kRow;                // the K (or V) rows of one tile
+constexpr int kIdSlots = 4;                      // page-table id slots per wave
+constexpr float kRescaleLog2 = 8.0f;
+constexpr int kMaxBatch = 1024;                  // requests per call on the MFMA path
+}  // namespace pf
+
+namespace pfc {  // two blocks per CU: 4 waves, K and V rings of two tiles each
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = kWaves * pf::kColsW;       // query columns per block
+constexpr int kKBase = 0;                        // K ring
+constexpr int kVBase = 2 * pf::kTile;            // V ring
+constexpr int kIdsBase = 4 * pf::kTile;          // per wave, kIdSlots tiles of ids
+constexpr int kLds = kIdsBase + kWaves * pf::kIdSlots * pf::kKT * 4;
+constexpr int kRowsW = pf::kKT / kWaves;         // rows of a tile this wave gathers
+constexpr int kGathers = kRowsW / 4;             // ... four per copy instruction
+static_assert(2 * kLds <= 160 * 1024, "two blocks must fit one CU's LDS");
+}  // namespace pfc
+
+namespace pfl {  // long chunks: one block per CU, 8 waves, a ring of 4 tiles
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = kWaves * pf::kColsW;       // query columns per block
 constexpr int kStages = 4;
 constexpr int kKBase = 0;                        // K tiles of the stages
-constexpr int kVBase = kStages * kTile;          // V tiles of the stages
-constexpr int kIdsBase = 2 * kStages * kTile;    // page-table ids: per wave, kIdSlots tiles
-constexpr int kIdSlots = 4;
-constexpr int kLds = kIdsBase + kWaves * kIdSlots * kKT * 4;
+constexpr int kVBase = kStages * pf::kTile;      // V tiles of the stages
+constexpr int kIdsBase = 2 * kStages * pf::kTile;  // page-table ids: per wave, kIdSlots tiles
+constexpr int kLds = kIdsBase + kWaves * pf::kIdSlots * pf::kKT * 4;
 constexpr int kAhead = kStages - 1;              // tiles gathered ahead of the compute
 constexpr int kIdsAhead = kStages + 1;           // tiles whose ids are copied ahead
 constexpr int kIdsPerTile = 1;                   // per wave and tile: 1 id copy ...
 constexpr int kVmemPerTile = kIdsPerTile + 4;    // ... and 4 gathers (none past the last tile)
-constexpr float kRescaleLog2 = 8.0f;
-constexpr int kMaxBatch = 1024;                  // requests per call on the MFMA path
-static_assert(kIdsAhead - kAhead < kIdSlots && kIdsAhead == kIdSlots + 1 && kAhead >= 2,
+static_assert(kIdsAhead - kAhead < pf::kIdSlots && kIdsAhead == pf::kIdSlots + 1 && kAhead >= 2,
               "an id slot is refilled only after its gathers were issued (the prologue relies on these values)");
-}  // namespace pf
+}  // namespace pfl
 
 MSGL_DEV floatx16_t mfma_32x32x16(const bf16x8_t &a, const bf16x8_t &b, const floatx16_t &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -155,40 +183,18 @@ MSGL_DEV void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Instruction order hint for one unit's main block: the first LDS reads up
-// front, then two MFMAs, about ten VALU instructions and the next LDS reads in
-// turn, so that the matrix core and the vector ALU work side by side instead
-// of in phases, and every MFMA finds its LDS operand already loaded (the
-// other orders are kept for tuning).
-#ifndef MSGL_PREFILL_SCHED
-#define MSGL_PREFILL_SCHED 4
-#endif
-#ifndef MSGL_PF_M
-#define MSGL_PF_M 2    // MFMAs per group
-#define MSGL_PF_V 10   // VALU instructions per group
-#define MSGL_PF_D 3    // LDS reads per group
-#define MSGL_PF_D0 8   // LDS reads ahead of the first group
-#endif
-template <int I, int N>
+// Instruction order hint for one unit's main block: D0 LDS reads up front,
+// then groups of M MFMAs, V VALU instructions and D LDS reads in turn, so
+// that the matrix core and the vector ALU work side by side instead of in
+// phases, and every MFMA finds its LDS operand already loaded.
+template <int M, int V, int D, int D0, int I = 0, int N = 16>
 MSGL_DEV void interleave_unit() {
-    if constexpr (MSGL_PREFILL_SCHED == 1 && I < N) {
-        __builtin_amdgcn_sched_group_barrier(0x100, I < 6 ? 2 : 1, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);              // VALU
-        interleave_unit<I + 1, N>();
-    } else if constexpr (MSGL_PREFILL_SCHED == 4 && I * MSGL_PF_M < N) {
-        if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, MSGL_PF_D0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, MSGL_PF_M, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, MSGL_PF_V, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, MSGL_PF_D, 0);
-        interleave_unit<I + 1, N>();
-    } else if constexpr (MSGL_PREFILL_SCHED >= 2 && MSGL_PREFILL_SCHED != 4 && I < N) {
-        constexpr int kValu = MSGL_PREFILL_SCHED == 2 ? 6 : MSGL_PREFILL_SCHED == 3 ? 4 : 5;
-        if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        interleave_unit<I + 1, N>();
+    if constexpr (I * M < N) {
+        if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, D0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+        interleave_unit<M, V, D, D0, I + 1, N>();
     }
 }
 
@@ -284,10 +290,10 @@ MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
 }
 
 template <int GQ>
-__global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
-    constexpr int BQ = pf::kCols / GQ;  // query tokens per block
-    constexpr int S = pf::kStages;
-    __shared__ __attribute__((aligned(1024))) char smem[pf::kLds];
+__global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(PrefillArgs a) {
+    constexpr int BQ = pfl::kCols / GQ;  // query tokens per block
+    constexpr int S = pfl::kStages;
+    __shared__ __attribute__((aligned(1024))) char smem[pfl::kLds];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
     // (keys past the block's last one read key 0's id: a real row whose scores
     // the causal mask removes)
     const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
-    const uint32_t ids_wave = lds0 + pf::kIdsBase + wave * pf::kIdSlots * pf::kKT * 4;
+    const uint32_t ids_wave = lds0 + pfl::kIdsBase + wave * pf::kIdSlots * pf::kKT * 4;
     auto copy_ids = [&](int t) __attribute__((always_inline)) {
         const int key = t * pf::kKT + lane;
         copy4_to_lds(pt, 4u * (uint32_t)(key < nkeys ? key : 0), ids_wave + (t % pf::kIdSlots) * pf::kKT * 4);
@@ -353,8 +359,8 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
             int s = lds_read_i32(ids + 16 * i);
             s = (uint32_t)s < num_slots ? s : 0;  // a malformed id stays inside the pool
             const uint32_t dst = lds0 + stage * pf::kTile + (8 * wave + 4 * i) * pf::kRow;
-            copy16_to_lds(kb[i] + (uint64_t)(uint32_t)s * row_bytes, dst + pf::kKBase);
-            copy16_to_lds(vb[i] + (uint64_t)(uint32_t)s * row_bytes, dst + pf::kVBase);
+            copy16_to_lds(kb[i] + (uint64_t)(uint32_t)s * row_bytes, dst + pfl::kKBase);
+            copy16_to_lds(vb[i] + (uint64_t)(uint32_t)s * row_bytes, dst + pfl::kVBase);
         }
     };
 
@@ -362,11 +368,11 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
     // ids of tile 4 copied once the slot of tile 0 has been read, then Q
 #pragma unroll
     for (int t = 0; t < pf::kIdSlots; ++t) copy_ids(t);
-    wait_vmcnt<pf::kIdSlots - pf::kAhead>();  // this wave's ids of tiles 0..2 (its own slots)
+    wait_vmcnt<pf::kIdSlots - pfl::kAhead>();  // this wave's ids of tiles 0..2 (its own slots)
     gather(0, 0);
     copy_ids(pf::kIdSlots);
 #pragma unroll
-    for (int t = 1; t < pf::kAhead; ++t)
+    for (int t = 1; t < pfl::kAhead; ++t)
         if (t < ntiles) gather(t, t);
     // Q^T operands: d-chunk dc holds dims 16*dc + 8*jj .. +7 of this column.
     // The empty asm below makes the compiler wait for them here, once; the
@@ -389,12 +395,12 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
         const int vrow = 4 * jj + ((lane >> 2) & 3);
         const int vch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
-        for (int dc = 0; dc < 8; ++dc) kaddr[dc] = lds0 + pf::kKBase + (lane & 31) * pf::kRow + (((2 * dc) ^ kx) << 4);
+        for (int dc = 0; dc < 8; ++dc) kaddr[dc] = lds0 + pfl::kKBase + (lane & 31) * pf::kRow + (((2 * dc) ^ kx) << 4);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int par = 0; par < 2; ++par)
-                vaddr[db][par] = lds0 + pf::kVBase + vrow * pf::kRow +
+                vaddr[db][par] = lds0 + pfl::kVBase + vrow * pf::kRow +
                                  (((4 * db + vch) ^ row_code(vrow + 8 * par)) << 4) + (lane & 1) * 8;
     }
 
@@ -480,7 +486,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
             // them past the rescale branch, away from the MFMAs they overlap)
             asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u), "v"(ls_u));
         }
-        if (has_scores && has_softmax) interleave_unit<0, 16>();
+        if (has_scores && has_softmax) interleave_unit<2, 10, 3, 8>();
         if (has_softmax && __any(mn != m)) {  // rare: rescale what units <= u accumulated
             const float alpha = fast_exp2(m - mn);
             lt *= alpha;
@@ -505,11 +511,11 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
         // this wave's copies of tile t+1 (and of the ids of tile t+S-1) are
         // done, the later ones may still be in flight; after the barrier
         // everyone's are, and every wave has finished reading tile t-1's stage
-        if (t + S - 2 < ntiles) wait_vmcnt<(S - 3) * pf::kVmemPerTile>();
-        else wait_vmcnt<(S - 3) * pf::kIdsPerTile>();  // some later tiles had no gathers: count only the id copies
+        if (t + S - 2 < ntiles) wait_vmcnt<(S - 3) * pfl::kVmemPerTile>();
+        else wait_vmcnt<(S - 3) * pfl::kIdsPerTile>();  // some later tiles had no gathers: count only the id copies
         lds_barrier();
-        copy_ids(t + pf::kIdsAhead);  // past the end: a harmless copy of key 0's id
-        if (t + pf::kAhead < ntiles) gather(t + pf::kAhead, (stage + pf::kAhead) % S);
+        copy_ids(t + pfl::kIdsAhead);  // past the end: a harmless copy of key 0's id
+        if (t + pfl::kAhead < ntiles) gather(t + pfl::kAhead, (stage + pfl::kAhead) % S);
         const int next = (stage + 1) % S;
         unit(2 * t, stage, next, true, true);
         unit(2 * t + 1, stage, next, true, true);
@@ -557,18 +563,291 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_mfma_kernel(PrefillAr
     }
 }
 
+// Two blocks per CU: 4 waves (128 query columns) and K and V rings of two
+// 64-key tiles each (68 KB of LDS), so that while one block waits (its
+// start, its gathers, the dispatch of the next block) the other computes.
+// At tile t the wave waits for all its copies and a barrier makes everyone's
+// visible (K of t+1, V of t, issued in tile t-1, and the ids of t+2 for this
+// tile's gathers); then it refills the stages tile t-1 used, K of t+2 and V of
+// t+1, copies the ids of t+3, and runs units 2t and 2t+1 as above.
+template <int GQ>
+__global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
+    constexpr int BQ = pfc::kCols / GQ;  // query tokens per block
+    __shared__ __attribute__((aligned(1024))) char smem[pfc::kLds];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int jj = lane >> 5;
+    const int G = a.kv_heads;
+
+    const int kvh = blockIdx.x % G;
+    const BlockItem item = a.batch <= 64    ? sorted_block<BQ, 1>(a, blockIdx.x / G, lane)
+                           : a.batch <= 256 ? sorted_block<BQ, 4>(a, blockIdx.x / G, lane)
+                                            : sorted_block<BQ, pf::kMaxBatch / 64>(a, blockIdx.x / G, lane);
+    const int b = __builtin_amdgcn_readfirstlane(item.b);
+    const int qb = __builtin_amdgcn_readfirstlane(item.qb);
+    if (b < 0) return;
+    const int L = (int)min((int64_t)a.seq_lens[b], a.row_stride);
+    const int C = a.cached_lens[b];
+    const int E = L - C;
+    const int t0 = qb * BQ;
+    if (qb < 0 || C < 0 || t0 >= E) return;
+    const int row0 = a.cu_q[b] + t0;
+    const int ntok = min(min(BQ, E - t0), a.total_q - row0);
+    if (ntok <= 0) return;
+    const int pos0 = C + t0;
+    const int nkeys = pos0 + ntok;
+    const int ntiles = (nkeys + pf::kKT - 1) / pf::kKT;
+
+    const int col = wave * pf::kColsW + (lane & 31);
+    const int tl = col / GQ;
+    const int hq = kvh * GQ + col % GQ;
+    const bool valid = tl < ntok;
+    const int tok = valid ? tl : ntok - 1;
+    const int pos = pos0 + tok;
+
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)smem;
+    const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
+    const uint32_t ids_wave = lds0 + pfc::kIdsBase + wave * pf::kIdSlots * pf::kKT * 4;
+    auto copy_ids = [&](int t) __attribute__((always_inline)) {
+        const int key = t * pf::kKT + lane;
+        copy4_to_lds(pt, 4u * (uint32_t)(key < nkeys ? key : 0), ids_wave + (t % pf::kIdSlots) * pf::kKT * 4);
+    };
+    const uint32_t num_slots = (uint32_t)a.num_slots;
+    const uint32_t row_bytes = (uint32_t)G * pf::kRow;
+    const int grp = lane >> 4;
+    const char *kb[pfc::kGathers], *vb[pfc::kGathers];
+#pragma unroll
+    for (int i = 0; i < pfc::kGathers; ++i) {
+        const uint32_t off =
+            (uint32_t)kvh * pf::kRow + (((lane & 15) ^ row_code(pfc::kRowsW * wave + 4 * i + grp)) << 4);
+        kb[i] = reinterpret_cast<const char *>(a.k_pool) + off;
+        vb[i] = reinterpret_cast<const char *>(a.v_pool) + off;
+    }
+    // this wave's rows R*w + 4i + l/16 of the K (or V) rows of tile t, into ring stage t % 2
+    auto gather = [&](int t, bool is_v) __attribute__((always_inline)) {
+        const uint32_t ids = ids_wave + (t % pf::kIdSlots) * pf::kKT * 4 + (pfc::kRowsW * wave + grp) * 4;
+        const uint32_t base = lds0 + (t & 1) * pf::kTile + (is_v ? pfc::kVBase : pfc::kKBase);
+        int sl[pfc::kGathers];
+#pragma unroll
+        for (int i = 0; i < pfc::kGathers; ++i) {
+            sl[i] = lds_read_i32(ids + 16 * i);
+            sl[i] = (uint32_t)sl[i] < num_slots ? sl[i] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < pfc::kGathers; ++i) {
+            const uint32_t dst = base + (pfc::kRowsW * wave + 4 * i) * pf::kRow;
+            copy16_to_lds((is_v ? vb[i] : kb[i]) + (uint64_t)(uint32_t)sl[i] * row_bytes, dst);
+        }
+    };
+
+    // prologue: ids of tiles 0..2, K of tiles 0 and 1, V of tile 0, then Q and a full wait
+#pragma unroll
+    for (int t = 0; t < 3; ++t) copy_ids(t);
+    wait_vmcnt<0>();
+    gather(0, false);
+    if (ntiles > 1) gather(1, false);
+    gather(0, true);
+    bf16x8_t qv[8];
+    const bf16_t *qp = reinterpret_cast<const bf16_t *>(a.q) +
+                       ((int64_t)(row0 + tok) * a.q_heads + hq) * pf::kD + 8 * jj;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) qv[dc] = __builtin_bit_cast(bf16x8_t, ld16(qp + 16 * dc));
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) asm volatile("" ::"v"(qv[dc]));
+    wait_vmcnt<0>();
+
+    uint32_t kaddr[8], vaddr[4][2];
+    {
+        const int kx = row_code(lane & 15) ^ jj;
+        const int vrow = 4 * jj + ((lane >> 2) & 3);
+        const int vch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int dc = 0; dc < 8; ++dc) kaddr[dc] = lds0 + pfc::kKBase + (lane & 31) * pf::kRow + (((2 * dc) ^ kx) << 4);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int par = 0; par < 2; ++par)
+                vaddr[db][par] = lds0 + pfc::kVBase + vrow * pf::kRow +
+                                 (((4 * db + vch) ^ row_code(vrow + 8 * par)) << 4) + (lane & 1) * 8;
+    }
+
+    floatx16_t acc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = floatx16_t{};
+    float m;
+    float lt = 0.0f;
+    float ls = 0.0f;
+    floatx16_t sc;
+    bf16x8_t pb[2];
+
+    auto scores = [&](int stage, int half) __attribute__((always_inline)) {
+        floatx16_t s = floatx16_t{};
+#pragma unroll
+        for (int dc = 0; dc < 8; ++dc)
+            s = mfma_32x32x16(lds_read16(kaddr[dc] + stage * pf::kTile + half * 32 * pf::kRow), qv[dc], s);
+        return s;
+    };
+    auto mask = [&](floatx16_t &s, int u) __attribute__((always_inline)) {
+        if (32 * u + 31 > pos0) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key = 32 * u + 8 * (e >> 2) + 4 * jj + (e & 3);
+                s[e] = key > pos ? -INFINITY : s[e];
+            }
+        }
+    };
+    auto column_max = [&](const floatx16_t &s) __attribute__((always_inline)) {
+        float mx = fmaxf(s[0], fmaxf(s[1], s[2]));
+#pragma unroll
+        for (int e = 3; e < 15; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+        mx = fmaxf(mx, s[15]);
+        return max_with_other_half(mx) * a.scale_log2;
+    };
+    auto weights = [&](const floatx16_t &s, float mu, bf16x8_t (&out)[2], float &sum, float &sum_rounded)
+        __attribute__((always_inline)) {
+        uint32_t pw[8];
+        sum = 0.0f;
+        sum_rounded = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, -mu));
+            const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, -mu));
+            pw[e >> 1] = pack_bf16x2(p0, p1);
+            sum += p0 + p1;
+            sum_rounded = dot2_bf16(pw[e >> 1], 0x3f803f80u, sum_rounded);
+        }
+        out[0] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        out[1] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+    };
+    auto pv = [&](int stage, int half) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            uint2 av[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                av[qq] = lds_read_tr16(vaddr[db][qq & 1] + stage * pf::kTile + half * 32 * pf::kRow +
+                                       8 * qq * pf::kRow);
+            acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(av[0].x, av[0].y, av[1].x, av[1].y)),
+                                    pb[0], acc[db]);
+            acc[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, make_uint4(av[2].x, av[2].y, av[3].x, av[3].y)),
+                                    pb[1], acc[db]);
+        }
+    };
+    auto unit = [&](int u, int stage, int next, bool has_scores, bool has_softmax) __attribute__((always_inline)) {
+        const int half = u & 1;
+        if (has_softmax) mask(sc, u + 1);
+        floatx16_t s_new;
+        if (has_scores) s_new = scores(next, half);
+        pv(stage, half);
+        float mn = m, lt_u = 0.0f, ls_u = 0.0f;
+        bf16x8_t pb_new[2];
+        if (has_softmax) {
+            const float mx = column_max(sc);
+            mn = mx > m + pf::kRescaleLog2 ? mx : m;
+            weights(sc, mn, pb_new, lt_u, ls_u);
+            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u), "v"(ls_u));
+        }
+        if (has_scores && has_softmax) interleave_unit<1, 5, 2, 8>();
+        if (has_softmax && __any(mn != m)) {
+            const float alpha = fast_exp2(m - mn);
+            lt *= alpha;
+            ls *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+        }
+        if (has_softmax) {
+            m = mn;
+            lt += lt_u;
+            ls += ls_u;
+            pb[0] = pb_new[0];
+            pb[1] = pb_new[1];
+        }
+        if (has_scores) sc = s_new;
+    };
+    // tile t < ntiles-1 (K of t+1 and V of t were copied in tile t-1): wait for
+    // every copy, then refill the ring stages tile t-1 used with K of t+2 and
+    // V of t+1 and copy the ids of t+3, then units 2t and 2t+1
+    auto tile = [&](int t, int stage) __attribute__((always_inline)) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        copy_ids(t + 3);  // past the end: a harmless copy of key 0's id
+        if (t + 2 < ntiles) gather(t + 2, false);
+        gather(t + 1, true);
+        const int next = stage ^ 1;
+        unit(2 * t, stage, next, true, true);
+        unit(2 * t + 1, stage, next, true, true);
+    };
+
+    lds_barrier();
+    {
+        floatx16_t s0 = scores(0, 0);
+        sc = scores(0, 1);
+        mask(s0, 0);
+        m = column_max(s0);
+        weights(s0, m, pb, lt, ls);
+    }
+    int t = 0;
+    for (; t + 2 <= ntiles - 1; t += 2) {
+        tile(t, 0);
+        tile(t + 1, 1);
+    }
+    if (t < ntiles - 1) {
+        tile(t, 0);
+        ++t;
+    }
+    // the last tile (V of ntiles-1 was copied in the tile before)
+    wait_vmcnt<0>();
+    lds_barrier();
+    const int last = (ntiles - 1) & 1;
+    unit(2 * ntiles - 2, last, 0, false, true);
+    unit(2 * ntiles - 1, last, 0, false, false);
+
+    lt = add_with_other_half(lt);
+    ls = add_with_other_half(ls);
+    if (valid) {
+        const float inv = 1.0f / ls;
+        bf16_t *op = reinterpret_cast<bf16_t *>(a.out) + ((int64_t)(row0 + tl) * a.q_heads + hq) * pf::kD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = db * 32 + 8 * i + 4 * jj;
+                *reinterpret_cast<uint2 *>(op + d0) =
+                    make_uint2(pack_bf16x2(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv),
+                               pack_bf16x2(acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv));
+            }
+        if (a.lse != nullptr && jj == 0) a.lse[(int64_t)(row0 + tl) * a.q_heads + hq] = (m + __log2f(lt)) * kLn2;
+    }
+}
+
 namespace {
+
+// Query blocks (times the kv heads) of a layout with BQ query tokens per block:
+// at most sum over requests of ceil(E_b / BQ).
+int64_t prefill_blocks(const PrefillArgs &a, int BQ) {
+    const int64_t nqb = (a.max_extend + BQ - 1) / BQ;
+    return std::min(nqb * a.batch, ((int64_t)a.total_q + (int64_t)a.batch * (BQ - 1)) / BQ) * a.kv_heads;
+}
 
 template <int GQ>
 hipError_t run_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
-    constexpr int BQ = pf::kCols / GQ;
-    // at most sum over requests of ceil(E_b / BQ) query blocks
-    const int64_t nqb = (a.max_extend + BQ - 1) / BQ;
-    const int64_t blocks = std::min(nqb * a.batch, ((int64_t)a.total_q + (int64_t)a.batch * (BQ - 1)) / BQ);
-    const int64_t grid = blocks * a.kv_heads;
+    // Requests of 2048 or more new tokens on average: long, uniform blocks,
+    // where the single-block layout's deeper ring keeps the matrix cores
+    // busier; otherwise block starts and the spread of block lengths weigh
+    // more, and two blocks per CU hide them.
+    const bool long_chunks = (int64_t)a.total_q >= 2048 * (int64_t)a.batch;
+    const int BQ = (long_chunks ? pfl::kCols : pfc::kCols) / GQ;
+    const int64_t grid = prefill_blocks(a, BQ);
     if (grid < 1) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_mfma_kernel<GQ>), dim3((unsigned)grid), dim3(pf::kThreads), 0, stream, a);
+    if (long_chunks)
+        hipLaunchKernelGGL((prefill_mfma_long_kernel<GQ>), dim3((unsigned)grid), dim3(pfl::kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((prefill_mfma_kernel<GQ>), dim3((unsigned)grid), dim3(pfc::kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -163,6 +163,16 @@ def test_ragged_prefill_beyond_mfma_batch(oracle_mod, runner, wl):
     assert max_abs(res.lse[idx], lse_ref) < 1e-3
 
 
+@pytest.mark.parametrize("H,G", [(16, 8), (32, 8)])
+def test_ragged_prefill_long_chunks(oracle_mod, runner, wl, H, G):
+    # 2048 or more new tokens per request: the single-block layout with the
+    # deeper ring serves the call; every row against the oracle
+    w = wl.ragged_prefill(device="cuda", n_req=2, e_lo=2048, e_hi=2300, c_lo=0, c_hi=300, num_slots=1 << 13,
+                          seed=49 + H, heads=dict(H=H, G=G, d=128))
+    assert w.num_tokens >= 2048 * w.bs
+    _full_check(oracle_mod, runner, w, rowsum_reqs=[0, 1])
+
+
 def test_ragged_prefill_v_ones_exact(runner, wl):
     w = wl.ragged_prefill(device="cuda", n_req=3, e_lo=30, e_hi=300, c_lo=0, c_hi=200, num_slots=1 << 11,
                           seed=46)
