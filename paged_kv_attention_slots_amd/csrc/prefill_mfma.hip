@@ -217,23 +217,41 @@ MSGL_DEV int wave_sum(int v) {
 struct BlockItem {
     int b;
     int qb;
+    int E;      // new tokens of request b
+    int C;      // its cached tokens
+    int q0;     // its first q row (cu_q[b])
+    int row;    // its page-table row (table_idx[b])
 };
 
 // NB = number of requests each lane keeps in registers (batch <= 64 NB); the
-// lengths are read once.
+// per-request values are read once, and the found request's are handed over
+// from the lane that holds them.  Up to 4 requests per lane the first q row
+// and page-table row come in the same round trip as the lengths; beyond, they
+// are read once the request is known (registers are scarcer there).
 template <int BQ, int NB>
 MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
-    // new and cached tokens of the lane's requests (no blocks when a request is malformed)
-    int E[NB], C[NB];
+    constexpr bool kAll = NB <= 4;
+    constexpr int NX = kAll ? NB : 1;
+    // new and cached tokens of the lane's requests (no blocks when a request is
+    // malformed), their first q rows and page-table rows
+    int E[NB], C[NB], Q0[NX], TI[NX];
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
         const int b = lane + 64 * k;
         E[k] = 0;
         C[k] = 0;
+        if (kAll) {
+            Q0[k % NX] = 0;
+            TI[k % NX] = 0;
+        }
         if (b < a.batch) {
             const int L = (int)min((int64_t)a.seq_lens[b], a.row_stride);
             C[k] = a.cached_lens[b];
             E[k] = C[k] < 0 ? 0 : L - C[k];
+            if (kAll) {
+                Q0[k % NX] = a.cu_q[b];
+                TI[k % NX] = a.table_idx[b];
+            }
         }
     }
     // first query block of a request with more than x key tiles (nb if none)
@@ -250,7 +268,7 @@ MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
             if (E[k] > 0) n += (E[k] + BQ - 1) / BQ - first_above(E[k], C[k], x);
         return wave_sum(n);
     };
-    if (count_above(0) <= r) return {-1, 0};
+    if (count_above(0) <= r) return {-1, 0, 0, 0, 0, 0};
     // tile count x of entry r: the largest x with more than r blocks of >= x tiles
     int most = 0;  // the most key tiles any block sees
 #pragma unroll
@@ -282,11 +300,17 @@ MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
         const unsigned long long hit = __ballot(k >= incl - c && k < incl);
         if (hit != 0) {
             const int src = __builtin_ctzll(hit);
-            return {__shfl(lane + 64 * j, src), __shfl(q0 + k - (incl - c), src)};
+            const int b = __shfl(lane + 64 * j, src);
+            if constexpr (kAll)
+                return {b, __shfl(q0 + k - (incl - c), src), __shfl(E[j], src), __shfl(C[j], src),
+                        __shfl(Q0[j % NX], src), __shfl(TI[j % NX], src)};
+            else
+                return {b, __shfl(q0 + k - (incl - c), src), __shfl(E[j], src), __shfl(C[j], src),
+                        a.cu_q[__builtin_amdgcn_readfirstlane(b)], a.table_idx[__builtin_amdgcn_readfirstlane(b)]};
         }
         k -= __shfl(incl, 63);
     }
-    return {-1, 0};
+    return {-1, 0, 0, 0, 0, 0};
 }
 
 template <int GQ>
@@ -309,12 +333,11 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
     const int b = __builtin_amdgcn_readfirstlane(item.b);
     const int qb = __builtin_amdgcn_readfirstlane(item.qb);
     if (b < 0) return;  // past the last query block: uniform over the block, before any barrier
-    const int L = (int)min((int64_t)a.seq_lens[b], a.row_stride);
-    const int C = a.cached_lens[b];
-    const int E = L - C;
+    const int C = __builtin_amdgcn_readfirstlane(item.C);
+    const int E = __builtin_amdgcn_readfirstlane(item.E);
     const int t0 = qb * BQ;
     if (qb < 0 || C < 0 || t0 >= E) return;
-    const int row0 = a.cu_q[b] + t0;
+    const int row0 = __builtin_amdgcn_readfirstlane(item.q0) + t0;
     const int ntok = min(min(BQ, E - t0), a.total_q - row0);
     if (ntok <= 0) return;
     const int pos0 = C + t0;         // position of the block's first token
@@ -333,7 +356,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
     // page-table ids: each wave copies all 64 ids of a tile into its own slot
     // (keys past the block's last one read key 0's id: a real row whose scores
     // the causal mask removes)
-    const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
+    const int32_t *pt = a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(item.row) * a.row_stride;
     const uint32_t ids_wave = lds0 + pfl::kIdsBase + wave * pf::kIdSlots * pf::kKT * 4;
     auto copy_ids = [&](int t) __attribute__((always_inline)) {
         const int key = t * pf::kKT + lane;
@@ -588,12 +611,11 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int b = __builtin_amdgcn_readfirstlane(item.b);
     const int qb = __builtin_amdgcn_readfirstlane(item.qb);
     if (b < 0) return;
-    const int L = (int)min((int64_t)a.seq_lens[b], a.row_stride);
-    const int C = a.cached_lens[b];
-    const int E = L - C;
+    const int C = __builtin_amdgcn_readfirstlane(item.C);
+    const int E = __builtin_amdgcn_readfirstlane(item.E);
     const int t0 = qb * BQ;
     if (qb < 0 || C < 0 || t0 >= E) return;
-    const int row0 = a.cu_q[b] + t0;
+    const int row0 = __builtin_amdgcn_readfirstlane(item.q0) + t0;
     const int ntok = min(min(BQ, E - t0), a.total_q - row0);
     if (ntok <= 0) return;
     const int pos0 = C + t0;
@@ -608,7 +630,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int pos = pos0 + tok;
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)smem;
-    const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
+    const int32_t *pt = a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(item.row) * a.row_stride;
     const uint32_t ids_wave = lds0 + pfc::kIdsBase + wave * pf::kIdSlots * pf::kKT * 4;
     auto copy_ids = [&](int t) __attribute__((always_inline)) {
         const int key = t * pf::kKT + lane;
