@@ -604,13 +604,14 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int jj = lane >> 5;
     const int G = a.kv_heads;
 
+    // block id = list entry * G + kv head: the query blocks longest first, no gaps
     const int kvh = blockIdx.x % G;
     const BlockItem item = a.batch <= 64    ? sorted_block<BQ, 1>(a, blockIdx.x / G, lane)
                            : a.batch <= 256 ? sorted_block<BQ, 4>(a, blockIdx.x / G, lane)
                                             : sorted_block<BQ, pf::kMaxBatch / 64>(a, blockIdx.x / G, lane);
     const int b = __builtin_amdgcn_readfirstlane(item.b);
     const int qb = __builtin_amdgcn_readfirstlane(item.qb);
-    if (b < 0) return;
+    if (b < 0) return;  // past the last query block: uniform over the block, before any barrier
     const int C = __builtin_amdgcn_readfirstlane(item.C);
     const int E = __builtin_amdgcn_readfirstlane(item.E);
     const int t0 = qb * BQ;
@@ -618,10 +619,11 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int row0 = __builtin_amdgcn_readfirstlane(item.q0) + t0;
     const int ntok = min(min(BQ, E - t0), a.total_q - row0);
     if (ntok <= 0) return;
-    const int pos0 = C + t0;
-    const int nkeys = pos0 + ntok;
+    const int pos0 = C + t0;         // position of the block's first token
+    const int nkeys = pos0 + ntok;   // keys 0 .. position of its last token
     const int ntiles = (nkeys + pf::kKT - 1) / pf::kKT;
 
+    // this lane's query column
     const int col = wave * pf::kColsW + (lane & 31);
     const int tl = col / GQ;
     const int hq = kvh * GQ + col % GQ;
@@ -630,6 +632,9 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int pos = pos0 + tok;
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)smem;
+    // page-table ids: each wave copies all 64 ids of a tile into its own slot
+    // (keys past the block's last one read key 0's id: a real row whose scores
+    // the causal mask removes)
     const int32_t *pt = a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(item.row) * a.row_stride;
     const uint32_t ids_wave = lds0 + pfc::kIdsBase + wave * pf::kIdSlots * pf::kKT * 4;
     auto copy_ids = [&](int t) __attribute__((always_inline)) {
@@ -647,7 +652,9 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
         kb[i] = reinterpret_cast<const char *>(a.k_pool) + off;
         vb[i] = reinterpret_cast<const char *>(a.v_pool) + off;
     }
-    // this wave's rows R*w + 4i + l/16 of the K (or V) rows of tile t, into ring stage t % 2
+    // this wave's rows R*w + 4i + l/16 (i < 4) of the K (or V) rows of tile t,
+    // into ring stage t % 2; lane l writes chunk position l%16 of its row, so
+    // it loads the chunk that the permutation puts there
     auto gather = [&](int t, bool is_v) __attribute__((always_inline)) {
         const uint32_t ids = ids_wave + (t % pf::kIdSlots) * pf::kKT * 4 + (pfc::kRowsW * wave + grp) * 4;
         const uint32_t base = lds0 + (t & 1) * pf::kTile + (is_v ? pfc::kVBase : pfc::kKBase);
@@ -655,7 +662,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
 #pragma unroll
         for (int i = 0; i < pfc::kGathers; ++i) {
             sl[i] = lds_read_i32(ids + 16 * i);
-            sl[i] = (uint32_t)sl[i] < num_slots ? sl[i] : 0;
+            sl[i] = (uint32_t)sl[i] < num_slots ? sl[i] : 0;  // a malformed id stays inside the pool
         }
 #pragma unroll
         for (int i = 0; i < pfc::kGathers; ++i) {
@@ -671,6 +678,8 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     gather(0, false);
     if (ntiles > 1) gather(1, false);
     gather(0, true);
+    // Q^T operands as in the single-block layout; the empty asm makes the
+    // compiler wait for them here, and the explicit wait covers the copies
     bf16x8_t qv[8];
     const bf16_t *qp = reinterpret_cast<const bf16_t *>(a.q) +
                        ((int64_t)(row0 + tok) * a.q_heads + hq) * pf::kD + 8 * jj;
@@ -680,6 +689,8 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     for (int dc = 0; dc < 8; ++dc) asm volatile("" ::"v"(qv[dc]));
     wait_vmcnt<0>();
 
+    // LDS read addresses of ring stage 0's first half, as in the single-block
+    // layout (stages and halves are immediate offsets)
     uint32_t kaddr[8], vaddr[4][2];
     {
         const int kx = row_code(lane & 15) ^ jj;
