@@ -358,7 +358,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this attention step has no cross-GPU path "
-              "(the design for sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "(each GPU would run it on its own share of heads or requests). Run with --gpus 1.",
+              file=sys.stderr)
         return 2
 
     import torch
