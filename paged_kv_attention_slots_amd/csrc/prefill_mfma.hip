@@ -453,9 +453,9 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
         }
     };
     auto column_max = [&](const floatx16_t &s) __attribute__((always_inline)) {
-        float mx = fmaxf(s[0], fmaxf(s[1], s[2]));
+        float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);  // a chain of three-input maxes
 #pragma unroll
-        for (int e = 3; e < 15; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+        for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, s[e]), s[e + 1]);
         mx = fmaxf(mx, s[15]);
         return max_with_other_half(mx) * a.scale_log2;  // raw scores: the scale is positive
     };
@@ -732,9 +732,9 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
         }
     };
     auto column_max = [&](const floatx16_t &s) __attribute__((always_inline)) {
-        float mx = fmaxf(s[0], fmaxf(s[1], s[2]));
+        float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);  // a chain of three-input maxes
 #pragma unroll
-        for (int e = 3; e < 15; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+        for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, s[e]), s[e + 1]);
         mx = fmaxf(mx, s[15]);
         return max_with_other_half(mx) * a.scale_log2;
     };
