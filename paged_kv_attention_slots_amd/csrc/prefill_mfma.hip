@@ -45,10 +45,10 @@
 // Softmax: log2 domain (scale times log2 e folded into one fma before exp2),
 // one running max per column per unit and lazy rescaling: the max only moves
 // when a unit's max exceeds it by more than 2^8, which keeps exp2 arguments
-// bounded and skips almost every rescale.  The output is normalised by the
-// sum of the bf16-rounded probabilities that the P.V product uses, so the
-// applied weights sum to one; the returned lse comes from an fp32 sum of the
-// unrounded weights.  Both sums are lane-partial and reduced once at the end.
+// bounded and skips almost every rescale.  One fp32 sum of the unrounded
+// weights, lane-partial and reduced once at the end, gives both the
+// normalisation and the returned lse.  The P.V product uses the weights
+// rounded to bf16, so the applied weights sum to one within 2^-9 relative.
 //
 // Block ids enumerate the query blocks of all requests densely, in decreasing
 // order of the keys they see (computed in the kernel from the lengths), so the
@@ -431,8 +431,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = floatx16_t{};
     float m;                          // running column max (log2 units; may lag by < 2^8)
-    float lt = 0.0f;                  // this lane's share of the running sum of the weights (for lse)
-    float ls = 0.0f;                  // ... and of the bf16-rounded weights (for normalising)
+    float lt = 0.0f;                  // this lane's share of the running sum of the weights
     floatx16_t sc;                    // raw scores of the unit whose softmax is next
     bf16x8_t pb[2];                   // weights of the unit whose P.V is next
 
@@ -459,19 +458,16 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
         mx = fmaxf(mx, s[15]);
         return max_with_other_half(mx) * a.scale_log2;  // raw scores: the scale is positive
     };
-    // weights exp2(s * scale - mu), rounded pairs for P.V, and their two sums
-    auto weights = [&](const floatx16_t &s, float mu, bf16x8_t (&out)[2], float &sum, float &sum_rounded)
-        __attribute__((always_inline)) {
+    // weights exp2(s * scale - mu), rounded pairs for P.V, and their sum
+    auto weights = [&](const floatx16_t &s, float mu, bf16x8_t (&out)[2], float &sum) __attribute__((always_inline)) {
         uint32_t pw[8];
         sum = 0.0f;
-        sum_rounded = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, -mu));
             const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, -mu));
             pw[e >> 1] = pack_bf16x2(p0, p1);
             sum += p0 + p1;
-            sum_rounded = dot2_bf16(pw[e >> 1], 0x3f803f80u, sum_rounded);  // the pair as P.V will use it
         }
         out[0] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
         out[1] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
@@ -499,21 +495,20 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
         floatx16_t s_new;
         if (has_scores) s_new = scores(next, half);
         pv(stage, half);
-        float mn = m, lt_u = 0.0f, ls_u = 0.0f;
+        float mn = m, lt_u = 0.0f;
         bf16x8_t pb_new[2];
         if (has_softmax) {
             const float mx = column_max(sc);
             mn = mx > m + pf::kRescaleLog2 ? mx : m;  // lazy: move the max only by more than 2^8
-            weights(sc, mn, pb_new, lt_u, ls_u);
+            weights(sc, mn, pb_new, lt_u);
             // keep the weights in this block (the compiler would otherwise sink
             // them past the rescale branch, away from the MFMAs they overlap)
-            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u), "v"(ls_u));
+            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u));
         }
         if (has_scores && has_softmax) interleave_unit<2, 10, 3, 8>();
         if (has_softmax && __any(mn != m)) {  // rare: rescale what units <= u accumulated
             const float alpha = fast_exp2(m - mn);
             lt *= alpha;
-            ls *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -522,7 +517,6 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
         if (has_softmax) {
             m = mn;
             lt += lt_u;
-            ls += ls_u;
             pb[0] = pb_new[0];
             pb[1] = pb_new[1];
         }
@@ -551,7 +545,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
         sc = scores(0, 1);
         mask(s0, 0);
         m = column_max(s0);  // key 0 is visible to every column: finite
-        weights(s0, m, pb, lt, ls);
+        weights(s0, m, pb, lt);
     }
     int t = 0;
     for (; t + S <= ntiles - 1; t += S) {
@@ -569,9 +563,8 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
     wait_vmcnt<0>();
 
     lt = add_with_other_half(lt);
-    ls = add_with_other_half(ls);
     if (valid) {
-        const float inv = 1.0f / ls;
+        const float inv = 1.0f / lt;
         bf16_t *op = reinterpret_cast<bf16_t *>(a.out) + ((int64_t)(row0 + tl) * a.q_heads + hq) * pf::kD;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -711,7 +704,6 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     for (int db = 0; db < 4; ++db) acc[db] = floatx16_t{};
     float m;
     float lt = 0.0f;
-    float ls = 0.0f;
     floatx16_t sc;
     bf16x8_t pb[2];
 
@@ -738,18 +730,15 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
         mx = fmaxf(mx, s[15]);
         return max_with_other_half(mx) * a.scale_log2;
     };
-    auto weights = [&](const floatx16_t &s, float mu, bf16x8_t (&out)[2], float &sum, float &sum_rounded)
-        __attribute__((always_inline)) {
+    auto weights = [&](const floatx16_t &s, float mu, bf16x8_t (&out)[2], float &sum) __attribute__((always_inline)) {
         uint32_t pw[8];
         sum = 0.0f;
-        sum_rounded = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, -mu));
             const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, -mu));
             pw[e >> 1] = pack_bf16x2(p0, p1);
             sum += p0 + p1;
-            sum_rounded = dot2_bf16(pw[e >> 1], 0x3f803f80u, sum_rounded);
         }
         out[0] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
         out[1] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
@@ -774,19 +763,18 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
         floatx16_t s_new;
         if (has_scores) s_new = scores(next, half);
         pv(stage, half);
-        float mn = m, lt_u = 0.0f, ls_u = 0.0f;
+        float mn = m, lt_u = 0.0f;
         bf16x8_t pb_new[2];
         if (has_softmax) {
             const float mx = column_max(sc);
             mn = mx > m + pf::kRescaleLog2 ? mx : m;
-            weights(sc, mn, pb_new, lt_u, ls_u);
-            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u), "v"(ls_u));
+            weights(sc, mn, pb_new, lt_u);
+            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u));
         }
         if (has_scores && has_softmax) interleave_unit<1, 5, 2, 8>();
         if (has_softmax && __any(mn != m)) {
             const float alpha = fast_exp2(m - mn);
             lt *= alpha;
-            ls *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -795,7 +783,6 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
         if (has_softmax) {
             m = mn;
             lt += lt_u;
-            ls += ls_u;
             pb[0] = pb_new[0];
             pb[1] = pb_new[1];
         }
@@ -821,7 +808,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
         sc = scores(0, 1);
         mask(s0, 0);
         m = column_max(s0);
-        weights(s0, m, pb, lt, ls);
+        weights(s0, m, pb, lt);
     }
     int t = 0;
     for (; t + 2 <= ntiles - 1; t += 2) {
@@ -840,9 +827,8 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     unit(2 * ntiles - 1, last, 0, false, false);
 
     lt = add_with_other_half(lt);
-    ls = add_with_other_half(ls);
     if (valid) {
-        const float inv = 1.0f / ls;
+        const float inv = 1.0f / lt;
         bf16_t *op = reinterpret_cast<bf16_t *>(a.out) + ((int64_t)(row0 + tl) * a.q_heads + hq) * pf::kD;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
