@@ -67,7 +67,7 @@ struct PrefillArgs {
     const int32_t *seq_lens;
     const int32_t *cached_lens;
     const int32_t *cu_q;
-    int64_t num_slots;
+    int64_t num_slots;  // slot ids outside [0, num_slots) read an in-pool slot (the last one on the MFMA path)
     int32_t batch;
     int32_t total_q;
     int32_t max_extend;

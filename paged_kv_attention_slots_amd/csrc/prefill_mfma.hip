@@ -365,7 +365,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
     // gathers: per tile this wave fills rows 8w + 4i + l/16 (i = 0, 1) of K and
     // V; lane l writes chunk position l%16 of its row, so it loads the chunk
     // that the permutation puts there
-    const uint32_t num_slots = (uint32_t)a.num_slots;
+    const uint32_t last_slot = (uint32_t)(min(a.num_slots, (int64_t)1 << 31) - 1);
     const uint32_t row_bytes = (uint32_t)G * pf::kRow;
     const int grp = lane >> 4;
     const char *kb[2], *vb[2];
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             int s = lds_read_i32(ids + 16 * i);
-            s = (uint32_t)s < num_slots ? s : 0;  // a malformed id stays inside the pool
+            s = (int)min((uint32_t)s, last_slot);  // a malformed id (negative or too large) reads the last slot
             const uint32_t dst = lds0 + stage * pf::kTile + (8 * wave + 4 * i) * pf::kRow;
             copy16_to_lds(kb[i] + (uint64_t)(uint32_t)s * row_bytes, dst + pfl::kKBase);
             copy16_to_lds(vb[i] + (uint64_t)(uint32_t)s * row_bytes, dst + pfl::kVBase);
@@ -634,7 +634,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
         const int key = t * pf::kKT + lane;
         copy4_to_lds(pt, 4u * (uint32_t)(key < nkeys ? key : 0), ids_wave + (t % pf::kIdSlots) * pf::kKT * 4);
     };
-    const uint32_t num_slots = (uint32_t)a.num_slots;
+    const uint32_t last_slot = (uint32_t)(min(a.num_slots, (int64_t)1 << 31) - 1);
     const uint32_t row_bytes = (uint32_t)G * pf::kRow;
     const int grp = lane >> 4;
     const char *kb[pfc::kGathers], *vb[pfc::kGathers];
@@ -655,7 +655,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
 #pragma unroll
         for (int i = 0; i < pfc::kGathers; ++i) {
             sl[i] = lds_read_i32(ids + 16 * i);
-            sl[i] = (uint32_t)sl[i] < num_slots ? sl[i] : 0;  // a malformed id stays inside the pool
+            sl[i] = (int)min((uint32_t)sl[i], last_slot);  // a malformed id (negative or too large) reads the last slot
         }
 #pragma unroll
         for (int i = 0; i < pfc::kGathers; ++i) {
