@@ -54,6 +54,8 @@ def _load():
         lib.oracle_attention.argtypes = [ctypes.c_int, I64, P, P, P, P, I64, P, P, P,
                                          I64, I64, I64, ctypes.c_double, P, P]
         lib.oracle_attention.restype = None
+        lib.oracle_rope.argtypes = [ctypes.c_int, P, I64, I64, I64, P, ctypes.c_double, P]
+        lib.oracle_rope.restype = None
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -140,6 +142,32 @@ def attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                              pt.shape[1], _ptr(q), _ptr(kp), _ptr(vp), H, G, d, float(scale),
                              _ptr(out), _ptr(lse))
     return out, lse
+
+
+def rope(x: torch.Tensor, positions: torch.Tensor, base: float) -> torch.Tensor:
+    """Rotary embedding of ``x`` ``[T, heads, head_dim]`` (fp32 or bf16) at
+    ``positions`` ``[T]``, in fp64 (pairs i and i + head_dim/2 turn by
+    ``positions[t] * base**(-2i/head_dim)``).  Returns a float64 tensor."""
+    x = _cpu(x)
+    pos = _cpu(positions).to(torch.int32)
+    T, heads, d = x.shape
+    assert d % 2 == 0 and pos.numel() == T and base > 0
+    out = torch.empty(T, heads, d, dtype=torch.float64)
+    _load().oracle_rope(_dtype_code(x), _ptr(x), T, heads, d, _ptr(pos), float(base), _ptr(out))
+    return out
+
+
+def rope_store_kv(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, v_pool: torch.Tensor,
+                  positions: torch.Tensor, out_loc: torch.Tensor, base: float):
+    """The layer's RoPE followed by the KV write: q and k turned by
+    ``rope`` and, at slot ``out_loc[t]``, the K pool gets the turned k row and
+    the V pool the v row.  Returns ``(q_rot, k_rot, v_pool')``: the turned
+    rows in fp64 and the V pool after the write (the K pool's written rows are
+    ``k_rot`` in the storage type, its other rows unchanged)."""
+    q_rot = rope(q, positions, base)
+    k_rot = rope(k_new, positions, base)
+    _, vp = store_kv(v_pool, v_pool, k_new, v_new, out_loc)
+    return q_rot, k_rot, vp
 
 
 def step(w, scale: Optional[float] = None):

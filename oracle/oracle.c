@@ -28,6 +28,19 @@
  *              scale defaults to 1/sqrt(head_dim) in the Python wrapper.
  *              Sums run in increasing j (and c) order.
  *
+ *   rope       Rotary position embedding of the new tokens' q and k, the step
+ *              the Mini-SGLang Engine article's per-layer pipeline runs between
+ *              the QKV projection and the KV write.  The pages give no formula;
+ *              this is the published rotary embedding (Su et al., "RoFormer",
+ *              section 3.2, the general form) with the pairing of the GPT-NeoX and
+ *              Qwen families: element i of a head is paired with element
+ *              i + d/2, and for a token at position p the pair turns by
+ *              a_i = p * base^(-2i/d), i = 0 .. d/2 - 1:
+ *                y[i]       = x[i] cos a_i - x[i + d/2] sin a_i
+ *                y[i + d/2] = x[i + d/2] cos a_i + x[i] sin a_i
+ *              Every head of the token (q heads and kv heads alike) turns by
+ *              the same angles.
+ *
  * Error behaviour: none; arguments are assumed valid (the Python wrapper
  * checks shapes before calling).
  */
@@ -145,6 +158,29 @@ void oracle_attention(int dtype, int64_t n_req, const int32_t *table_idx,
         free(s);
     }
     free(req_of);
+}
+
+/*
+ * x   [T, heads, head_dim] in storage type dtype; positions [T];
+ * out [T, heads, head_dim] double.  head_dim is even.
+ */
+void oracle_rope(int dtype, const void *x, int64_t num_tokens, int64_t heads,
+                 int64_t head_dim, const int32_t *positions, double base, double *out)
+{
+    int64_t half = head_dim / 2;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        double p = (double)positions[t];
+        for (int64_t h = 0; h < heads; ++h) {
+            int64_t row = (t * heads + h) * head_dim;
+            for (int64_t i = 0; i < half; ++i) {
+                double a = p * pow(base, -2.0 * (double)i / (double)head_dim);
+                double x1 = orc_load(x, row + i, dtype);
+                double x2 = orc_load(x, row + i + half, dtype);
+                out[row + i] = x1 * cos(a) - x2 * sin(a);
+                out[row + i + half] = x2 * cos(a) + x1 * sin(a);
+            }
+        }
+    }
 }
 
 /* thread control for timing; n <= 0 leaves the OpenMP default */

@@ -37,6 +37,15 @@ MUTANTS = {
                           "memcpy(v_pool + (int64_t)out_loc[t] * row_bytes, k_new"),
     "query_row_of_first_token": ("orc_one(dtype, q, (t * q_heads + h) * head_dim",
                                  "orc_one(dtype, q, (q_start[b] * q_heads + h) * head_dim"),
+    "rope_sign": ("out[row + i] = x1 * cos(a) - x2 * sin(a);", "out[row + i] = x1 * cos(a) + x2 * sin(a);"),
+    "rope_adjacent_pairs": ("double x2 = orc_load(x, row + i + half, dtype);",
+                            "double x2 = orc_load(x, row + (i + 1) % head_dim, dtype);"),
+    "rope_frequency_exponent": ("pow(base, -2.0 * (double)i / (double)head_dim)",
+                                "pow(base, -1.0 * (double)i / (double)head_dim)"),
+    "rope_one_angle": ("double a = p * pow(base, -2.0 * (double)i / (double)head_dim);", "double a = p;"),
+    "rope_token_index_as_position": ("double p = (double)positions[t];", "double p = (double)t;"),
+    "rope_swapped_halves": ("out[row + i + half] = x2 * cos(a) + x1 * sin(a);",
+                            "out[row + i + half] = x1 * cos(a) + x2 * sin(a);"),
 }
 
 CHECKS = [
@@ -48,6 +57,11 @@ CHECKS = [
     ("store_kv", pins.test_store_kv_definition),
     ("bf16", pins.test_bf16_widening_is_exact),
     ("length_one", pins.test_length_one_returns_v),
+    ("rope_identity", pins.test_rope_position_zero_is_identity),
+    ("rope_complex", pins.test_rope_two_dims_is_complex_rotation),
+    ("rope_frequencies", pins.test_rope_four_dims_frequencies),
+    ("rope_lengths", pins.test_rope_keeps_pair_lengths),
+    ("rope_distance", pins.test_rope_scores_depend_on_distance_only),
 ]
 
 
@@ -68,7 +82,8 @@ def test_mutant_is_caught(tmp_path, oracle_mod, name):
     so = _build_mutant(tmp_path, name)
     real = oracle_pkg._load()
     lib = ctypes.CDLL(so)
-    for fn in ("oracle_store_kv", "oracle_attention", "oracle_set_threads", "oracle_num_threads"):
+    for fn in ("oracle_store_kv", "oracle_attention", "oracle_rope", "oracle_set_threads",
+               "oracle_num_threads"):
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         getattr(lib, fn).restype = getattr(real, fn).restype
     oracle_pkg._lib = lib

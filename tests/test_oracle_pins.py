@@ -18,6 +18,7 @@ operand, a missing max subtraction) fails at least one of them:
 * store_kv: written rows equal the new rows, every other slot is unchanged.
 """
 
+import cmath
 import math
 
 import numpy as np
@@ -275,3 +276,95 @@ def test_bf16_widening_is_exact(oracle_mod):
                                     torch.tensor([0, 1], dtype=torch.int32))
     assert out[0, 0, :4].tolist() == [1.0 + 2 ** -7, -3.5, 2 ** -120, 65280.0]
     assert lse[0, 0].item() == 0.0
+
+
+# ---------------------------------------------------------------------------
+# Rotary embedding (the step before the KV write in the layer's pipeline).
+# Pins: position 0 is the identity; with two dimensions the embedding is the
+# complex rotation (x0 + i x1) e^{ip}; with four dimensions and base 10^4 the
+# two pairs turn by p and p / 100 (angles worked out by hand); every pair
+# keeps its length; q.k depends only on the distance between positions.
+
+def _rope_inputs(T=6, heads=3, d=8, seed=7, dtype=torch.float32, max_pos=40000):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, heads, d, generator=g).to(dtype)
+    pos = torch.randint(0, max_pos, (T,), generator=g, dtype=torch.int32)
+    return x, pos
+
+
+def test_rope_position_zero_is_identity(oracle_mod):
+    x, _ = _rope_inputs(dtype=torch.bfloat16, d=128)
+    out = oracle_mod.rope(x, torch.zeros(x.shape[0], dtype=torch.int32), 1e6)
+    assert torch.equal(out, x.double())
+
+
+def test_rope_two_dims_is_complex_rotation(oracle_mod):
+    x, pos = _rope_inputs(d=2)
+    out = oracle_mod.rope(x, pos, 12345.0)  # the only frequency is base**0 = 1
+    for t in range(x.shape[0]):
+        for h in range(x.shape[1]):
+            z = complex(float(x[t, h, 0]), float(x[t, h, 1])) * cmath.exp(1j * int(pos[t]))
+            assert abs(float(out[t, h, 0]) - z.real) < 1e-12
+            assert abs(float(out[t, h, 1]) - z.imag) < 1e-12
+
+
+def test_rope_four_dims_frequencies(oracle_mod):
+    # d = 4, base = 10^4: elements (0, 2) turn by p radians, (1, 3) by p / 100
+    x, _ = _rope_inputs(T=5, heads=2, d=4)
+    pos = torch.tensor([0, 1, 2, 50, 314], dtype=torch.int32)
+    out = oracle_mod.rope(x, pos, 1e4)
+    for t in range(5):
+        p = int(pos[t])
+        for h in range(2):
+            for i, angle in ((0, float(p)), (1, p / 100.0)):
+                z = complex(float(x[t, h, i]), float(x[t, h, i + 2])) * cmath.exp(1j * angle)
+                assert abs(float(out[t, h, i]) - z.real) < 1e-12, (t, h, i)
+                assert abs(float(out[t, h, i + 2]) - z.imag) < 1e-12, (t, h, i)
+
+
+def test_rope_keeps_pair_lengths(oracle_mod):
+    x, pos = _rope_inputs(T=16, heads=4, d=128, dtype=torch.bfloat16)
+    out = oracle_mod.rope(x, pos, 1e6)
+    xd = x.double()
+    n_in = xd[..., :64] ** 2 + xd[..., 64:] ** 2
+    n_out = out[..., :64] ** 2 + out[..., 64:] ** 2
+    assert torch.allclose(n_out, n_in, rtol=1e-12, atol=1e-14)
+    assert not torch.allclose(out, xd)
+
+
+def test_rope_scores_depend_on_distance_only(oracle_mod):
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(1, 1, 64, generator=g, dtype=torch.float32)
+    k = torch.randn(1, 1, 64, generator=g, dtype=torch.float32)
+
+    def score(m, n):
+        rq = oracle_mod.rope(q, torch.tensor([m], dtype=torch.int32), 1e4)
+        rk = oracle_mod.rope(k, torch.tensor([n], dtype=torch.int32), 1e4)
+        return float((rq * rk).sum())
+
+    bound = 1e-9 * float(q.double().norm() * k.double().norm())
+    for m, n in ((7, 3), (3, 7), (100, 0), (5, 5)):
+        ref = score(m, n)
+        for shift in (1, 17, 1000, 30000):
+            assert abs(score(m + shift, n + shift) - ref) < bound, (m, n, shift)
+    assert abs(score(5, 5) - float((q.double() * k.double()).sum())) < bound
+    assert abs(score(7, 3) - score(3, 7)) > 1e-3  # the sign of the distance matters
+
+
+def test_rope_store_kv_definition(oracle_mod):
+    g = torch.Generator().manual_seed(3)
+    T, H, G, d, S = 5, 4, 2, 64, 32
+    q = torch.randn(T, H, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(T, G, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(T, G, d, generator=g).to(torch.bfloat16)
+    vp = torch.randn(S, G, d, generator=g).to(torch.bfloat16)
+    pos = torch.tensor([0, 9, 4, 31, 2], dtype=torch.int32)
+    loc = torch.tensor([3, 17, 0, 31, 8], dtype=torch.int32)
+    q_rot, k_rot, vp2 = oracle_mod.rope_store_kv(q, k, v, vp, pos, loc, 1e6)
+    assert torch.equal(q_rot, oracle_mod.rope(q, pos, 1e6))
+    assert torch.equal(k_rot, oracle_mod.rope(k, pos, 1e6))
+    assert torch.equal(q_rot[0], q[0].double()) and torch.equal(k_rot[0], k[0].double())
+    assert torch.equal(vp2[loc.long()].view(torch.int16), v.view(torch.int16))
+    untouched = torch.ones(S, dtype=torch.bool)
+    untouched[loc.long()] = False
+    assert torch.equal(vp2[untouched].view(torch.int16), vp[untouched].view(torch.int16))
