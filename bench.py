@@ -89,6 +89,17 @@ def store_bytes(w) -> int:
     return 2 * 2 * w.num_tokens * w.kv_heads * w.head_dim * e + 4 * w.num_tokens
 
 
+def rope_store_bytes(w) -> int:
+    """Algorithmic HBM bytes of one fused RoPE + KV write: q and k read and
+    written once each, v read and written once, a position and a slot id per
+    token."""
+    e = w.dtype.itemsize
+    return 2 * w.num_tokens * (w.q_heads + 2 * w.kv_heads) * w.head_dim * e + 8 * w.num_tokens
+
+
+ROPE_BASE = 1e6  # Qwen3's rotary base
+
+
 def prefill_flops(w) -> float:
     """Matrix flops of the unmasked (query, key) pairs: 2 matmuls x 2 flop x d per pair and head."""
     ext = (w.seq_lens - w.cached_lens).double()
@@ -460,6 +471,22 @@ def main() -> int:
     torch.cuda.synchronize()
     pattn_ms = ka.elapsed_time(kb) / args.kernel_iters
 
+    # the next step on the layer's path: RoPE of q and k fused with the KV write,
+    # on the decode batch and on the prefill batch (back-to-back launches)
+    log(f"timing {args.kernel_iters} fused RoPE + KV-write launches per batch")
+    rope = {}
+    for tag, w in (("decode_bs256", w4), ("prefill_8req", w3)):
+        q_rot = torch.empty_like(w.q)
+
+        def rope_call(w=w, q_rot=q_rot):
+            _lib.msgl_rope_store_kv(q_rot, w.q, w.k_pool, w.v_pool, w.k_new, w.v_new, w.positions, w.out_loc,
+                                    ROPE_BASE, stream=stream)
+
+        r_ms = _time_stream(rope_call, stream, args.kernel_iters)
+        r_gbs = rope_store_bytes(w) / (r_ms * 1e-3) / 1e9
+        rope[tag] = {"tokens": w.num_tokens, "ms": round(r_ms, 4), "GBs": round(r_gbs, 1),
+                     "frac_hbm": round(r_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": rope_store_bytes(w)}
+
     dbytes = decode_bytes(w4)
     sbytes = store_bytes(w4)
     flops3 = prefill_flops(w3)
@@ -529,6 +556,7 @@ def main() -> int:
         "prefill_attn_ms": round(pattn_ms, 4),
         "prefill_attn_tflops": round(pattn_tflops, 2),
         "prefill_attn_frac_of_bf16_peak": round(pattn_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+        "rope_store_kv": rope,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode attention (split + merge), eager, bs 256",

@@ -12,8 +12,8 @@
  *
  * Conventions shared by every call
  * --------------------------------
- * Pointers named *_pool, q, out, lse, k_new, v_new, page_table, table_idx,
- * seq_lens, cached_lens, cu_q, out_loc and workspace are DEVICE pointers owned
+ * Pointers named *_pool, q, q_out, out, lse, k_new, v_new, page_table, table_idx,
+ * seq_lens, cached_lens, cu_q, positions, out_loc and workspace are DEVICE pointers owned
  * by the caller; the library never frees or retains them (except a captured
  * graph, which records them; see msgl_decode_graph_create).  `stream` is a
  * hipStream_t passed as void* (NULL = the null stream).  Calls only enqueue
@@ -88,6 +88,34 @@ msgl_status msgl_store_kv(void *k_pool, void *v_pool, int64_t num_slots, int32_t
                           int32_t head_dim, msgl_dtype dtype, const void *k_new,
                           const void *v_new, const int32_t *out_loc, int32_t num_tokens,
                           void *stream);
+
+/*
+ * msgl_rope_store_kv - rotary position embedding of the new q and k rows,
+ * fused with the KV write (the layer's RoPE and KV-write steps, in that
+ * order, from the Mini-SGLang Engine article's per-layer pipeline).
+ * For every new token t at position p = positions[t] and every head, element
+ * i < head_dim/2 pairs with element i + head_dim/2 and the pair turns by
+ * a_i = p * rope_base^(-2 i / head_dim) (RoFormer, section 3.2, general form,
+ * half-split pairing as in the GPT-NeoX and Qwen models):
+ *   y[i] = x[i] cos a_i - x[i + d/2] sin a_i,
+ *   y[i + d/2] = x[i + d/2] cos a_i + x[i] sin a_i.
+ * Writes q_out[t] = rotated q[t] ([q_heads, head_dim] per token; q_out may
+ * equal q for an in-place update), k_pool[out_loc[t]] = rotated k_new[t], and
+ * v_pool[out_loc[t]] = v_new[t] bit for bit.  k_new is not modified.  The
+ * angles are computed in double precision and the rotation in float32, then
+ * rounded once (round to nearest even) to the storage type.
+ * positions[t] is normally cached_len + i for the request's i-th new token.
+ * out_loc follows msgl_store_kv's rules; a token whose out_loc lies outside
+ * [0, num_slots) still has its q rotated but writes no pool row.
+ * rope_base must be positive and finite (Qwen3 uses 1e6).  q_heads in
+ * [1, 256]; kv_heads, head_dim and dtype as for msgl_store_kv.
+ * num_tokens == 0 is a no-op.
+ */
+msgl_status msgl_rope_store_kv(void *q_out, const void *q, void *k_pool, void *v_pool,
+                               int64_t num_slots, int32_t q_heads, int32_t kv_heads,
+                               int32_t head_dim, msgl_dtype dtype, const void *k_new,
+                               const void *v_new, const int32_t *positions, const int32_t *out_loc,
+                               int32_t num_tokens, double rope_base, void *stream);
 
 /*
  * Decode attention: one query token per request, at position seq_lens[b] - 1

@@ -29,7 +29,8 @@ MSGL_BF16 = 1
 
 # Every symbol include/msgl.h declares.
 EXPORTS = (
-    "msgl_last_error", "msgl_version", "msgl_store_kv", "msgl_decode_workspace_bytes",
+    "msgl_last_error", "msgl_version", "msgl_store_kv", "msgl_rope_store_kv",
+    "msgl_decode_workspace_bytes",
     "msgl_decode_attn", "msgl_prefill_attn", "msgl_decode_graph_create", "msgl_graph_launch",
     "msgl_graph_destroy", "msgl_validate_batch",
 )
@@ -52,6 +53,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msgl_version.restype = ctypes.c_int
     lib.msgl_store_kv.restype = st
     lib.msgl_store_kv.argtypes = [P, P, I64, I32, I32, st, P, P, P, I32, P]
+    lib.msgl_rope_store_kv.restype = st
+    lib.msgl_rope_store_kv.argtypes = [P, P, P, P, I64, I32, I32, I32, st, P, P, P, P, I32,
+                                       ctypes.c_double, P]
     lib.msgl_decode_workspace_bytes.restype = SZ
     lib.msgl_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.msgl_decode_attn.restype = st
@@ -124,6 +128,19 @@ def msgl_store_kv(k_pool, v_pool, k_new, v_new, out_loc, stream=None) -> None:
     S, G, d = k_pool.shape
     _check(lib.msgl_store_kv(_p(k_pool), _p(v_pool), S, G, d, _dt(k_pool), _p(k_new), _p(v_new),
                              _p(_i32(out_loc)), out_loc.numel(), _stream(stream)))
+
+
+def msgl_rope_store_kv(q_out, q, k_pool, v_pool, k_new, v_new, positions, out_loc,
+                       rope_base: float, stream=None) -> None:
+    T, H, d = q.shape
+    S, G, _ = k_pool.shape
+    if q_out.shape != q.shape or k_new.shape != (T, G, d) or v_new.shape != (T, G, d):
+        raise ValueError("q_out, k_new and v_new must match q [T, H, d] and the pools' [G, d]")
+    if positions.numel() != T or out_loc.numel() != T:
+        raise ValueError("positions and out_loc need one entry per token")
+    _check(lib.msgl_rope_store_kv(_p(q_out), _p(q), _p(k_pool), _p(v_pool), S, H, G, d, _dt(k_pool),
+                                  _p(k_new), _p(v_new), _p(_i32(positions)), _p(_i32(out_loc)), T,
+                                  float(rope_base), _stream(stream)))
 
 
 def msgl_decode_workspace_bytes(batch: int, q_heads: int, head_dim: int, max_seq_len: int,

@@ -3,6 +3,7 @@
 // validator.  Nothing here allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <new>
@@ -166,6 +167,38 @@ msgl_status msgl_store_kv(void *k_pool, void *v_pool, int64_t num_slots, int32_t
                                                      v_new, out_loc, num_tokens),
                                           static_cast<hipStream_t>(stream)),
                     "store_kv launch");
+}
+
+msgl_status msgl_rope_store_kv(void *q_out, const void *q, void *k_pool, void *v_pool,
+                               int64_t num_slots, int32_t q_heads, int32_t kv_heads,
+                               int32_t head_dim, msgl_dtype dtype, const void *k_new,
+                               const void *v_new, const int32_t *positions, const int32_t *out_loc,
+                               int32_t num_tokens, double rope_base, void *stream) {
+    msgl_status s = check_store(k_pool, v_pool, num_slots, kv_heads, head_dim, dtype, k_new, v_new,
+                                out_loc, num_tokens);
+    if (s != MSGL_OK) return s;
+    if (q_heads < 1 || q_heads > 256) return fail(MSGL_INVALID_ARG, "q_heads %d out of range [1, 256]", q_heads);
+    if (!(rope_base > 0.0) || !std::isfinite(rope_base))
+        return fail(MSGL_INVALID_ARG, "rope_base %g is not a positive finite number", rope_base);
+    if (num_tokens == 0) return ok();
+    if (!q_out || !q || !positions) return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    msgl::RopeStoreKvArgs a;
+    a.q_out = q_out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.positions = positions;
+    a.out_loc = out_loc;
+    a.num_slots = num_slots;
+    a.num_tokens = num_tokens;
+    a.q_heads = q_heads;
+    a.kv_heads = kv_heads;
+    a.head_dim = head_dim;
+    a.base = rope_base;
+    return from_hip(msgl::launch_rope_store_kv(a, static_cast<msgl::DType>(dtype), static_cast<hipStream_t>(stream)),
+                    "rope_store_kv launch");
 }
 
 size_t msgl_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim,

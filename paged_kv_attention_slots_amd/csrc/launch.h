@@ -31,6 +31,23 @@ struct StoreKvArgs {
     int64_t num_slots;  // rows with an out_loc outside [0, num_slots) are skipped
 };
 
+struct RopeStoreKvArgs {
+    void *q_out;       // [num_tokens, q_heads, head_dim]; may equal q
+    const void *q;
+    void *k_pool;
+    void *v_pool;
+    const void *k_new;
+    const void *v_new;
+    const int32_t *positions;
+    const int32_t *out_loc;
+    int64_t num_slots;  // rows with an out_loc outside [0, num_slots) are not written
+    int32_t num_tokens;
+    int32_t q_heads;
+    int32_t kv_heads;
+    int32_t head_dim;
+    double base;        // rotary base (theta)
+};
+
 struct DecodeArgs {
     void *out;
     float *lse;
@@ -79,6 +96,7 @@ struct PrefillArgs {
 size_t decode_workspace_bytes(int batch, int q_heads, int head_dim, int max_seq_len, int chunk);
 
 hipError_t launch_store_kv(const StoreKvArgs &a, hipStream_t stream);
+hipError_t launch_rope_store_kv(const RopeStoreKvArgs &a, DType dtype, hipStream_t stream);
 // prepare_only resolves the cached device queries and launches nothing (call
 // it before capturing the launch into a graph).
 hipError_t launch_decode(const DecodeArgs &a, DType dtype, int head_dim, hipStream_t stream,

@@ -1,0 +1,100 @@
+// rope_store_kv: rotary position embedding of the step's new q and k rows,
+// fused with the KV write.
+//
+// The Mini-SGLang Engine article lists a layer's work as QKV projection,
+// RoPE, KV write, attention.  This kernel does the middle two in one pass over
+// the new rows: q is turned (in place allowed), k is turned and written
+// straight into the K pool at out_loc, v is copied into the V pool.  The k row
+// is read once and written once, instead of being turned into a temporary and
+// copied by store_kv afterwards.
+//
+// Rotation (RoFormer, section 3.2, general form, with the half-split pairing
+// of the GPT-NeoX and Qwen models): element i of a head pairs with element
+// i + d/2, and at position p the pair turns by a_i = p * base^(-2i/d):
+//   y[i]       = x[i] cos a_i - x[i + d/2] sin a_i
+//   y[i + d/2] = x[i + d/2] cos a_i + x[i] sin a_i
+// All heads of a token, q and kv alike, turn by the same angles.
+//
+// Layout of the work: one block per token (grid-stride over tokens).  The
+// d/2 angles of the token are computed once, in double precision (pow and
+// sincos), rounded to float and kept in LDS; every head of the token then
+// uses them.  One work item is a pair of 16-byte vectors (the same offset in
+// both halves of one head): consecutive threads take consecutive vectors, so
+// a wave reads and writes whole 128-byte lines.  The rotation is float32 FMA
+// arithmetic, rounded once to the storage type.  V rows are copied bit for
+// bit.  HBM-bound: per token, q, k and v are each read and written once.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace msgl {
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_store_kv_kernel(RopeStoreKvArgs a) {
+    constexpr int kEpl = Store<T>::kEpl;  // elements per 16-byte vector
+    __shared__ float2 cs[128];            // (cos a_i, sin a_i), i < head_dim / 2
+    const int half = a.head_dim / 2;
+    const int hv = half / kEpl;  // vectors per half head
+    const int n_rot = (a.q_heads + a.kv_heads) * hv;
+    const int row_vec = a.kv_heads * a.head_dim / kEpl;  // vectors per V row
+    const int n_items = n_rot + row_vec;
+    for (int t = blockIdx.x; t < a.num_tokens; t += gridDim.x) {
+        if ((int)threadIdx.x < half) {
+            const int i = threadIdx.x;
+            const double ang = (double)a.positions[t] * pow(a.base, -2.0 * i / a.head_dim);
+            double s, c;
+            sincos(ang, &s, &c);
+            cs[i] = make_float2((float)c, (float)s);
+        }
+        __syncthreads();
+        const int64_t slot = a.out_loc[t];
+        const bool slot_ok = slot >= 0 && slot < a.num_slots;  // never write out of bounds
+        for (int it = threadIdx.x; it < n_items; it += blockDim.x) {
+            if (it < n_rot) {
+                const int head = it / hv;
+                const int j = it - head * hv;
+                const T *src;
+                T *dst;
+                if (head < a.q_heads) {
+                    const int64_t off = ((int64_t)t * a.q_heads + head) * a.head_dim;
+                    src = static_cast<const T *>(a.q) + off;
+                    dst = static_cast<T *>(a.q_out) + off;
+                } else {
+                    if (!slot_ok) continue;
+                    const int kh = head - a.q_heads;
+                    src = static_cast<const T *>(a.k_new) + ((int64_t)t * a.kv_heads + kh) * a.head_dim;
+                    dst = static_cast<T *>(a.k_pool) + (slot * a.kv_heads + kh) * a.head_dim;
+                }
+                float x1[kEpl], x2[kEpl], y1[kEpl], y2[kEpl];
+                Store<T>::widen(ld16(src + j * kEpl), x1);
+                Store<T>::widen(ld16(src + half + j * kEpl), x2);
+#pragma unroll
+                for (int e = 0; e < kEpl; ++e) {
+                    const float2 r = cs[j * kEpl + e];
+                    y1[e] = fmaf(x1[e], r.x, -x2[e] * r.y);
+                    y2[e] = fmaf(x2[e], r.x, x1[e] * r.y);
+                }
+                st16(dst + j * kEpl, Store<T>::narrow(y1));
+                st16(dst + half + j * kEpl, Store<T>::narrow(y2));
+            } else if (slot_ok) {
+                const int v = it - n_rot;
+                const uint4 x = ld16_nt(static_cast<const uint4 *>(a.v_new) + (int64_t)t * row_vec + v);
+                static_cast<uint4 *>(a.v_pool)[slot * row_vec + v] = x;
+            }
+        }
+        __syncthreads();  // the next token overwrites cs
+    }
+}
+
+hipError_t launch_rope_store_kv(const RopeStoreKvArgs &a, DType dtype, hipStream_t stream) {
+    if (a.num_tokens == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)(a.num_tokens < 65536 ? a.num_tokens : 65536);
+    if (dtype == kBF16)
+        hipLaunchKernelGGL(rope_store_kv_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(rope_store_kv_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace msgl

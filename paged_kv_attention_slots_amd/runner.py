@@ -65,3 +65,14 @@ def run_step(w: Workload, chunk: int = 0, with_lse: bool = True, in_place: bool 
     else:
         out, lse = prefill_attn(w, kp, vp, with_lse=with_lse)
     return StepResult(out, lse, kp, vp)
+
+
+def rope_store_kv(w: Workload, k_pool, v_pool, rope_base: float, q_out=None, stream=None):
+    """The layer's RoPE fused with the KV write: returns the rotated q (a new
+    tensor unless ``q_out`` is given; ``q_out=w.q`` rotates in place); the
+    rotated k rows and the v rows land in the pools at ``w.out_loc``."""
+    if q_out is None:
+        q_out = torch.empty_like(w.q)
+    _lib.msgl_rope_store_kv(q_out, w.q, k_pool, v_pool, w.k_new, w.v_new, w.positions, w.out_loc,
+                            rope_base, stream=stream)
+    return q_out

@@ -60,6 +60,29 @@ def test_store_kv_argument_checks(L):
     assert lib.msgl_store_kv(None, None, 100, 8, 128, 1, None, None, None, 0, None) == L.MSGL_OK
 
 
+def test_rope_store_kv_argument_checks(L):
+    lib = L.lib
+
+    def call(q_out=FAKE, q=FAKE, k=FAKE, v=FAKE, S=100, H=32, G=8, d=128, dt=1, kn=FAKE, vn=FAKE,
+             pos=FAKE, loc=FAKE, T=4, base=1e6):
+        return lib.msgl_rope_store_kv(q_out, q, k, v, S, H, G, d, dt, kn, vn, pos, loc, T, base, None)
+
+    assert call(d=96) == L.MSGL_UNSUPPORTED and "head_dim" in L.msgl_last_error()
+    assert call(dt=5) == L.MSGL_UNSUPPORTED
+    assert call(H=0) == L.MSGL_INVALID_ARG and "q_heads" in L.msgl_last_error()
+    assert call(base=0.0) == L.MSGL_INVALID_ARG and "rope_base" in L.msgl_last_error()
+    assert call(base=-1e4) == L.MSGL_INVALID_ARG
+    assert call(base=float("inf")) == L.MSGL_INVALID_ARG
+    assert call(base=float("nan")) == L.MSGL_INVALID_ARG
+    assert call(pos=None) == L.MSGL_INVALID_ARG and "NULL" in L.msgl_last_error()
+    assert call(q_out=None) == L.MSGL_INVALID_ARG
+    assert call(k=None) == L.MSGL_INVALID_ARG
+    assert call(T=-1) == L.MSGL_INVALID_ARG
+    assert call(S=0) == L.MSGL_INVALID_ARG
+    # zero tokens is a no-op that needs no pointers and no GPU
+    assert call(None, None, None, None, kn=None, vn=None, pos=None, loc=None, T=0) == L.MSGL_OK
+
+
 def _decode(L, **over):
     a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, S=1000, pt=FAKE, W=4096, tix=FAKE, sl=FAKE,
              bs=4, H=32, G=8, d=128, ps=1, msl=4096, chunk=0, scale=0.088, dt=1, ws=FAKE, wsb=1 << 30)
