@@ -56,6 +56,8 @@ def _load():
         lib.oracle_attention.restype = None
         lib.oracle_rope.argtypes = [ctypes.c_int, P, I64, I64, I64, P, ctypes.c_double, P]
         lib.oracle_rope.restype = None
+        lib.oracle_vocab_embed.argtypes = [P, I64, I64, I64, P, I64, P]
+        lib.oracle_vocab_embed.restype = None
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -168,6 +170,22 @@ def rope_store_kv(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, v_p
     k_rot = rope(k_new, positions, base)
     _, vp = store_kv(v_pool, v_pool, k_new, v_new, out_loc)
     return q_rot, k_rot, vp
+
+
+def vocab_embed(weight: torch.Tensor, ids: torch.Tensor, vocab_start: int = 0) -> torch.Tensor:
+    """Embedding rows of ``ids`` from a vocabulary shard: ``weight`` ``[rows,
+    hidden]`` holds the rows of ids ``vocab_start .. vocab_start + rows - 1``;
+    other ids give zero rows.  Returns a new CPU tensor ``[T, hidden]`` in
+    ``weight``'s dtype (rows copied bit for bit)."""
+    wt = _cpu(weight)
+    idx = _cpu(ids).to(torch.int32)
+    assert wt.dim() == 2
+    # poisoned, so that a row the C code left unwritten shows as NaN
+    out = torch.full((idx.numel(), wt.shape[1]), float("nan"), dtype=wt.dtype)
+    row_bytes = wt.shape[1] * wt.element_size()
+    _load().oracle_vocab_embed(_ptr(wt), wt.shape[0], row_bytes, int(vocab_start), _ptr(idx),
+                               idx.numel(), _ptr(out))
+    return out
 
 
 def step(w, scale: Optional[float] = None):

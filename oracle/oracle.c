@@ -41,6 +41,17 @@
  *              Every head of the token (q heads and kv heads alike) turns by
  *              the same angles.
  *
+ *   vocab_embed  Vocabulary indexing, the small custom kernel the Stage 4
+ *              milestone's table pairs with the KV write: the embedding rows
+ *              of the step's token ids.  Under tensor parallelism each rank
+ *              holds the rows [vocab_start, vocab_start + rows) of the table
+ *              (the table "What each chapter adds": several cards read the
+ *              weights together); a token id outside that range gives a zero
+ *              row, so the ranks' outputs sum to the full table's rows:
+ *                out[t] = weight[ids[t] - vocab_start]  if the id is in range
+ *                out[t] = 0                             otherwise.
+ *              A row is copied bit for bit.
+ *
  * Error behaviour: none; arguments are assumed valid (the Python wrapper
  * checks shapes before calling).
  */
@@ -180,6 +191,23 @@ void oracle_rope(int dtype, const void *x, int64_t num_tokens, int64_t heads,
                 out[row + i + half] = x2 * cos(a) + x1 * sin(a);
             }
         }
+    }
+}
+
+/*
+ * weight [rows, row_bytes] (any storage type, copied as bytes); ids [T];
+ * out [T, row_bytes].
+ */
+void oracle_vocab_embed(const uint8_t *weight, int64_t rows, int64_t row_bytes,
+                        int64_t vocab_start, const int32_t *ids, int64_t num_tokens,
+                        uint8_t *out)
+{
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        int64_t r = (int64_t)ids[t] - vocab_start;
+        if (r >= 0 && r < rows)
+            memcpy(out + t * row_bytes, weight + r * row_bytes, (size_t)row_bytes);
+        else
+            memset(out + t * row_bytes, 0, (size_t)row_bytes);
     }
 }
 

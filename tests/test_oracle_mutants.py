@@ -46,6 +46,9 @@ MUTANTS = {
     "rope_token_index_as_position": ("double p = (double)positions[t];", "double p = (double)t;"),
     "rope_swapped_halves": ("out[row + i + half] = x2 * cos(a) + x1 * sin(a);",
                             "out[row + i + half] = x1 * cos(a) + x2 * sin(a);"),
+    "vocab_range_inclusive_end": ("if (r >= 0 && r < rows)", "if (r >= 0 && r <= rows)"),
+    "vocab_no_start_offset": ("int64_t r = (int64_t)ids[t] - vocab_start;", "int64_t r = (int64_t)ids[t];"),
+    "vocab_stale_rows": ("            memset(out + t * row_bytes, 0, (size_t)row_bytes);", "            ;"),
 }
 
 CHECKS = [
@@ -62,6 +65,9 @@ CHECKS = [
     ("rope_frequencies", pins.test_rope_four_dims_frequencies),
     ("rope_lengths", pins.test_rope_keeps_pair_lengths),
     ("rope_distance", pins.test_rope_scores_depend_on_distance_only),
+    ("vocab_hand", pins.test_vocab_embed_hand_worked),
+    ("vocab_full", pins.test_vocab_embed_full_table_is_embedding),
+    ("vocab_shards", lambda o: pins.test_vocab_embed_shards_sum_to_full_table(o, 3)),
 ]
 
 
@@ -82,8 +88,8 @@ def test_mutant_is_caught(tmp_path, oracle_mod, name):
     so = _build_mutant(tmp_path, name)
     real = oracle_pkg._load()
     lib = ctypes.CDLL(so)
-    for fn in ("oracle_store_kv", "oracle_attention", "oracle_rope", "oracle_set_threads",
-               "oracle_num_threads"):
+    for fn in ("oracle_store_kv", "oracle_attention", "oracle_rope", "oracle_vocab_embed",
+               "oracle_set_threads", "oracle_num_threads"):
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         getattr(lib, fn).restype = getattr(real, fn).restype
     oracle_pkg._lib = lib

@@ -368,3 +368,54 @@ def test_rope_store_kv_definition(oracle_mod):
     untouched = torch.ones(S, dtype=torch.bool)
     untouched[loc.long()] = False
     assert torch.equal(vp2[untouched].view(torch.int16), vp[untouched].view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# vocabulary indexing (the embedding rows of the step's token ids, sharded by
+# vocabulary range as under tensor parallelism)
+# --------------------------------------------------------------------------
+
+
+def test_vocab_embed_hand_worked(oracle_mod):
+    # a shard holding ids 2..5 of the vocabulary: rows 10*r + (0, 1)
+    # (a view of a larger table: the row after the shard is real memory, so a
+    # range check that lets id 6 through reads 99s rather than garbage)
+    w = torch.tensor([[0.0, 1.0], [10.0, 11.0], [20.0, 21.0], [30.0, 31.0], [99.0, 99.0]])[:4]
+    ids = torch.tensor([1, 2, 3, 5, 6, -1, 4], dtype=torch.int32)
+    out = oracle_mod.vocab_embed(w, ids, vocab_start=2)
+    expect = torch.tensor([[0.0, 0.0], [0.0, 1.0], [10.0, 11.0], [30.0, 31.0], [0.0, 0.0], [0.0, 0.0],
+                           [20.0, 21.0]])
+    assert torch.equal(out, expect)
+
+
+def test_vocab_embed_full_table_is_embedding(oracle_mod):
+    g = torch.Generator().manual_seed(21)
+    w = torch.randn(1000, 64, generator=g).to(torch.bfloat16)
+    ids = torch.randint(0, 1000, (300,), generator=g, dtype=torch.int32)
+    out = oracle_mod.vocab_embed(w, ids)
+    ref = torch.nn.functional.embedding(ids.long(), w)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("shards", [2, 3, 4])
+def test_vocab_embed_shards_sum_to_full_table(oracle_mod, shards):
+    """Tensor-parallel split of the vocabulary: exactly one shard holds each
+    id, so the shards' outputs are the full rows there and zero elsewhere,
+    and they sum (all-reduce) to the full table's rows."""
+    g = torch.Generator().manual_seed(22)
+    V, hid = 997, 32
+    w = torch.randn(V, hid, generator=g)
+    bounds = [V * i // shards for i in range(shards + 1)]
+    edges = [x for i in range(shards) for x in (bounds[i], bounds[i + 1] - 1)]  # each shard's first and last id
+    ids = torch.cat([torch.randint(0, V, (257,), generator=g, dtype=torch.int32),
+                     torch.tensor(edges, dtype=torch.int32)])
+    full = oracle_mod.vocab_embed(w, ids)
+    total = torch.zeros_like(full, dtype=torch.float64)
+    owners = torch.zeros(ids.numel(), dtype=torch.int64)
+    for i in range(shards):
+        part = oracle_mod.vocab_embed(w[bounds[i]:bounds[i + 1]], ids, vocab_start=bounds[i])
+        nz = (part != 0).any(dim=1)
+        owners += nz.long()
+        total += part.double()
+    assert torch.equal(total, full.double())
+    assert bool((owners == 1).all())  # randn rows have no all-zero row
