@@ -123,7 +123,7 @@ def _find(dirname, suffix):
     raise FileNotFoundError(f"no *{suffix} under {dirname}")
 
 
-def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes):
+def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes, rope_bytes=None):
     """Write the committed text summaries from rocprofv3 output directories:
     the kernel-trace statistics of the bench command, and the decode kernels'
     HBM bytes per launch from FETCH_SIZE / WRITE_SIZE runs, scaled by what the
@@ -195,6 +195,36 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes)
         f"source_hash = {decode_source_hash()}",
     ]
     with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    if rope_bytes:
+        summarize_rope_traffic(fetch_dir, write_dir, command, f_scale, w_scale, rope_bytes)
+
+
+def summarize_rope_traffic(fetch_dir, write_dir, command, f_scale, w_scale, rope_bytes):
+    """HBM bytes per launch of the fused RoPE + KV-write kernel, per batch (the
+    bench launches it on the decode batch and on the prefill batch; the
+    dispatches are told apart by their grid size, smaller grid first)."""
+    def groups(dirname, counter):
+        out = {}
+        for r in _read_csv(_find(dirname, "counter_collection.csv")):
+            if r["Counter_Name"] == counter and "rope_store_kv_kernel" in r["Kernel_Name"]:
+                out.setdefault(int(r["Grid_Size"]), []).append(float(r["Counter_Value"]) * 1024.0)
+        return out
+
+    fetch, write = groups(fetch_dir, "FETCH_SIZE"), groups(write_dir, "WRITE_SIZE")
+    lines = ["# HBM traffic of one fused RoPE + KV-write launch (rope_store_kv_kernel), per batch",
+             f"# command (two runs): rocprofv3 --pmc FETCH_SIZE | --pmc WRITE_SIZE -- {command}",
+             "# counters per dispatch (KiB -> bytes), averaged, scaled by the plain-copy factors below",
+             f"copy_fetch_scale = {f_scale:.4f}", f"copy_write_scale = {w_scale:.4f}"]
+    for (tag, algo), grid in zip(sorted(rope_bytes.items(), key=lambda kv: kv[1]), sorted(fetch)):
+        fb = sum(fetch[grid]) / len(fetch[grid]) * f_scale
+        wb = sum(write.get(grid, [0.0])) / max(1, len(write.get(grid, []))) * w_scale
+        lines += [f"{tag}.grid_threads = {grid}", f"{tag}.dispatches_averaged = {len(fetch[grid])}",
+                  f"{tag}.fetch_bytes = {fb:.0f}", f"{tag}.write_bytes = {wb:.0f}",
+                  f"{tag}.algorithmic_bytes_per_launch = {algo}",
+                  f"{tag}.traffic_over_algorithmic = {(fb + wb) / algo:.4f}"]
+    with open(os.path.join(PROFILE_DIR, "rope_store_kv_qwen3_traffic.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -348,8 +378,13 @@ def main() -> int:
     if len(sys.argv) > 1 and sys.argv[1] == "--sweep":
         return sweep(int(sys.argv[2]) if len(sys.argv) > 2 else 20)
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
-        # bench.py --summarize-profiles STATS_DIR FETCH_DIR WRITE_DIR ALGO_BYTES "COMMAND"
-        summarize_profiles(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[6], int(sys.argv[5]))
+        # bench.py --summarize-profiles STATS_DIR FETCH_DIR WRITE_DIR ALGO_BYTES "COMMAND" [BENCH_JSON]
+        rope_bytes = None
+        if len(sys.argv) > 7:  # the bench line gives the RoPE kernel's algorithmic bytes per batch
+            with open(sys.argv[7]) as f:
+                rec = json.loads([ln for ln in f if ln.startswith("{")][-1])
+            rope_bytes = {k: v["bytes_per_launch"] for k, v in rec["rope_store_kv"].items()}
+        summarize_profiles(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[6], int(sys.argv[5]), rope_bytes)
         return 0
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,6 +522,20 @@ def main() -> int:
         rope[tag] = {"tokens": w.num_tokens, "ms": round(r_ms, 4), "GBs": round(r_gbs, 1),
                      "frac_hbm": round(r_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": rope_store_bytes(w)}
 
+    # vocabulary indexing on the Qwen3-8B table (151936 x 4096 bf16): the mixed
+    # step's 4288 new tokens and a decode batch of 256
+    log(f"timing {args.kernel_iters} vocabulary-indexing launches per batch")
+    vocab = {}
+    for tag, n in (("tokens4288", 4288), ("decode_bs256", 256)):
+        vb = wl.vocab_batch(device=dev, num_tokens=n)
+        e_out = torch.empty(n, vb.hidden, dtype=vb.weight.dtype, device=dev)
+        v_ms = _time_stream(lambda: _lib.msgl_vocab_embed(e_out, vb.weight, vb.ids, vb.vocab_start, stream=stream),
+                            stream, args.kernel_iters)
+        vbytes = 2 * n * vb.hidden * vb.weight.element_size() + 4 * n
+        vocab[tag] = {"tokens": n, "ms": round(v_ms, 4), "GBs": round(vbytes / (v_ms * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(vbytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": vbytes}
+        del vb, e_out
+
     dbytes = decode_bytes(w4)
     sbytes = store_bytes(w4)
     flops3 = prefill_flops(w3)
@@ -557,6 +606,7 @@ def main() -> int:
         "prefill_attn_tflops": round(pattn_tflops, 2),
         "prefill_attn_frac_of_bf16_peak": round(pattn_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
         "rope_store_kv": rope,
+        "vocab_embed": vocab,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode attention (split + merge), eager, bs 256",

@@ -13,7 +13,7 @@
  * Conventions shared by every call
  * --------------------------------
  * Pointers named *_pool, q, q_out, out, lse, k_new, v_new, page_table, table_idx,
- * seq_lens, cached_lens, cu_q, positions, out_loc and workspace are DEVICE pointers owned
+ * seq_lens, cached_lens, cu_q, positions, out_loc, weight, ids and workspace are DEVICE pointers owned
  * by the caller; the library never frees or retains them (except a captured
  * graph, which records them; see msgl_decode_graph_create).  `stream` is a
  * hipStream_t passed as void* (NULL = the null stream).  Calls only enqueue
@@ -116,6 +116,23 @@ msgl_status msgl_rope_store_kv(void *q_out, const void *q, void *k_pool, void *v
                                int32_t head_dim, msgl_dtype dtype, const void *k_new,
                                const void *v_new, const int32_t *positions, const int32_t *out_loc,
                                int32_t num_tokens, double rope_base, void *stream);
+
+/*
+ * msgl_vocab_embed - vocabulary indexing: the embedding rows of the step's
+ * token ids (the small custom kernel the Stage 4 milestone's table names next
+ * to the KV write).  `weight` [vocab_rows, hidden] holds the rows of the
+ * vocabulary ids vocab_start .. vocab_start + vocab_rows - 1 (one rank's
+ * shard under tensor parallelism; vocab_start 0 and the whole table on one
+ * GPU).  For t in [0, num_tokens): out[t] = weight[ids[t] - vocab_start],
+ * copied bit for bit, when the id lies in the shard, else a row of zeros, so
+ * the ranks' outputs sum to the full table's rows.  out is [num_tokens,
+ * hidden].  hidden * element size must be a multiple of 16 bytes (else
+ * MSGL_UNSUPPORTED); vocab_rows >= 1 and vocab_start >= 0 (else
+ * MSGL_INVALID_ARG).  Any int32 id is allowed.  num_tokens == 0 is a no-op.
+ */
+msgl_status msgl_vocab_embed(void *out, const void *weight, int64_t vocab_start, int64_t vocab_rows,
+                             int32_t hidden, msgl_dtype dtype, const int32_t *ids, int32_t num_tokens,
+                             void *stream);
 
 /*
  * Decode attention: one query token per request, at position seq_lens[b] - 1

@@ -29,7 +29,7 @@ MSGL_BF16 = 1
 
 # Every symbol include/msgl.h declares.
 EXPORTS = (
-    "msgl_last_error", "msgl_version", "msgl_store_kv", "msgl_rope_store_kv",
+    "msgl_last_error", "msgl_version", "msgl_store_kv", "msgl_rope_store_kv", "msgl_vocab_embed",
     "msgl_decode_workspace_bytes",
     "msgl_decode_attn", "msgl_prefill_attn", "msgl_decode_graph_create", "msgl_graph_launch",
     "msgl_graph_destroy", "msgl_validate_batch",
@@ -56,6 +56,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msgl_rope_store_kv.restype = st
     lib.msgl_rope_store_kv.argtypes = [P, P, P, P, I64, I32, I32, I32, st, P, P, P, P, I32,
                                        ctypes.c_double, P]
+    lib.msgl_vocab_embed.restype = st
+    lib.msgl_vocab_embed.argtypes = [P, P, I64, I64, I32, st, P, I32, P]
     lib.msgl_decode_workspace_bytes.restype = SZ
     lib.msgl_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.msgl_decode_attn.restype = st
@@ -141,6 +143,14 @@ def msgl_rope_store_kv(q_out, q, k_pool, v_pool, k_new, v_new, positions, out_lo
     _check(lib.msgl_rope_store_kv(_p(q_out), _p(q), _p(k_pool), _p(v_pool), S, H, G, d, _dt(k_pool),
                                   _p(k_new), _p(v_new), _p(_i32(positions)), _p(_i32(out_loc)), T,
                                   float(rope_base), _stream(stream)))
+
+
+def msgl_vocab_embed(out, weight, ids, vocab_start: int = 0, stream=None) -> None:
+    rows, hidden = weight.shape
+    if out.shape != (ids.numel(), hidden) or out.dtype != weight.dtype:
+        raise ValueError("out must be [num_tokens, hidden] in weight's dtype")
+    _check(lib.msgl_vocab_embed(_p(out), _p(weight), int(vocab_start), rows, hidden, _dt(weight),
+                                _p(_i32(ids)), ids.numel(), _stream(stream)))
 
 
 def msgl_decode_workspace_bytes(batch: int, q_heads: int, head_dim: int, max_seq_len: int,

@@ -201,6 +201,30 @@ msgl_status msgl_rope_store_kv(void *q_out, const void *q, void *k_pool, void *v
                     "rope_store_kv launch");
 }
 
+msgl_status msgl_vocab_embed(void *out, const void *weight, int64_t vocab_start, int64_t vocab_rows,
+                             int32_t hidden, msgl_dtype dtype, const int32_t *ids, int32_t num_tokens,
+                             void *stream) {
+    if (dtype != MSGL_F32 && dtype != MSGL_BF16) return fail(MSGL_UNSUPPORTED, "dtype %d not supported", (int)dtype);
+    if (hidden < 1) return fail(MSGL_INVALID_ARG, "hidden %d < 1", hidden);
+    const int64_t row_bytes = (int64_t)hidden * elem_bytes(dtype);
+    if (row_bytes % 16 != 0)
+        return fail(MSGL_UNSUPPORTED, "row of %lld bytes is not a multiple of 16", (long long)row_bytes);
+    if (vocab_rows < 1) return fail(MSGL_INVALID_ARG, "vocab_rows %lld < 1", (long long)vocab_rows);
+    if (vocab_start < 0) return fail(MSGL_INVALID_ARG, "vocab_start %lld < 0", (long long)vocab_start);
+    if (num_tokens < 0) return fail(MSGL_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+    if (num_tokens == 0) return ok();
+    if (!out || !weight || !ids) return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    msgl::VocabEmbedArgs a;
+    a.out = out;
+    a.weight = weight;
+    a.ids = ids;
+    a.vocab_start = vocab_start;
+    a.rows = vocab_rows;
+    a.row_vec = (int32_t)(row_bytes / 16);
+    a.num_tokens = num_tokens;
+    return from_hip(msgl::launch_vocab_embed(a, static_cast<hipStream_t>(stream)), "vocab_embed launch");
+}
+
 size_t msgl_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim,
                                    int32_t max_seq_len, int32_t chunk) {
     if (batch < 0 || q_heads < 1 || head_dim < 1 || max_seq_len < 1) return 0;

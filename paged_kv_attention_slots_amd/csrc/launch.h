@@ -48,6 +48,16 @@ struct RopeStoreKvArgs {
     double base;        // rotary base (theta)
 };
 
+struct VocabEmbedArgs {
+    void *out;            // [num_tokens, row_vec * 16 bytes]
+    const void *weight;   // [rows, row_vec * 16 bytes]
+    const int32_t *ids;   // [num_tokens]
+    int64_t vocab_start;  // vocabulary id of weight's row 0
+    int64_t rows;
+    int32_t row_vec;      // 16-byte vectors per row
+    int32_t num_tokens;
+};
+
 struct DecodeArgs {
     void *out;
     float *lse;
@@ -97,6 +107,7 @@ size_t decode_workspace_bytes(int batch, int q_heads, int head_dim, int max_seq_
 
 hipError_t launch_store_kv(const StoreKvArgs &a, hipStream_t stream);
 hipError_t launch_rope_store_kv(const RopeStoreKvArgs &a, DType dtype, hipStream_t stream);
+hipError_t launch_vocab_embed(const VocabEmbedArgs &a, hipStream_t stream);
 // prepare_only resolves the cached device queries and launches nothing (call
 // it before capturing the launch into a graph).
 hipError_t launch_decode(const DecodeArgs &a, DType dtype, int head_dim, hipStream_t stream,

@@ -52,6 +52,7 @@ _MUL2 = 0x846CA68B
 STREAM_K = 1
 STREAM_V = 2
 STREAM_Q = 3
+STREAM_EMBED = 1 << 20  # vocabulary table values (a stream no layer's K/V/Q uses)
 
 
 def _mul32(x: torch.Tensor, c: int) -> torch.Tensor:
@@ -640,3 +641,43 @@ def layer_history_values(step: MixedStep, layer: int, request: int, positions: t
     rows = base + positions.long().cpu()
     return gen_rows(w.seed, stream, rows, w.kv_heads * w.head_dim, 1.0, w.dtype, "cpu").view(
         -1, w.kv_heads, w.head_dim)
+
+
+# ----------------------------------------------------------------------------
+# vocabulary indexing
+# ----------------------------------------------------------------------------
+
+QWEN3_VOCAB = 151936
+QWEN3_8B_HIDDEN = 4096
+
+
+@dataclasses.dataclass
+class VocabBatch:
+    name: str
+    weight: torch.Tensor   # [rows, hidden]: the vocabulary ids vocab_start .. vocab_start + rows - 1
+    vocab_start: int
+    vocab_size: int        # of the whole (unsharded) vocabulary
+    ids: torch.Tensor      # int32 [T]
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.ids.numel())
+
+    @property
+    def hidden(self) -> int:
+        return int(self.weight.shape[1])
+
+
+def vocab_batch(seed: int = 1006, device="cpu", num_tokens: int = 4288, vocab: int = QWEN3_VOCAB,
+                hidden: int = QWEN3_8B_HIDDEN, shards: int = 1, rank: int = 0,
+                dtype: torch.dtype = torch.bfloat16, std: float = 0.02) -> VocabBatch:
+    """Token ids of one step (uniform over the whole vocabulary) and one rank's
+    shard of an embedding table: rows [vocab * rank // shards, vocab * (rank+1)
+    // shards) of a table whose row r holds stream values r * hidden .. (r+1) *
+    hidden - 1 (N(0, std^2) quantiles).  Defaults: the Qwen3-8B table (151936 x
+    4096, bf16) and the 4288 new tokens of the mixed step."""
+    rng = np.random.default_rng(seed)
+    ids = torch.from_numpy(rng.integers(0, vocab, size=num_tokens).astype(np.int32)).to(device)
+    lo, hi = vocab * rank // shards, vocab * (rank + 1) // shards
+    weight = gen_rows(seed, STREAM_EMBED, torch.arange(lo, hi, dtype=torch.int64), hidden, std, dtype, device)
+    return VocabBatch(f"vocab-{vocab}x{hidden}-tp{shards}r{rank}", weight, lo, vocab, ids)

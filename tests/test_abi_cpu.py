@@ -60,6 +60,23 @@ def test_store_kv_argument_checks(L):
     assert lib.msgl_store_kv(None, None, 100, 8, 128, 1, None, None, None, 0, None) == L.MSGL_OK
 
 
+def test_vocab_embed_argument_checks(L):
+    lib = L.lib
+
+    def call(out=FAKE, w=FAKE, start=0, rows=1000, hid=4096, dt=1, ids=FAKE, T=4):
+        return lib.msgl_vocab_embed(out, w, start, rows, hid, dt, ids, T, None)
+
+    assert call(hid=4) == L.MSGL_UNSUPPORTED and "16" in L.msgl_last_error()  # 8-byte bf16 rows
+    assert call(dt=3) == L.MSGL_UNSUPPORTED
+    assert call(hid=0) == L.MSGL_INVALID_ARG
+    assert call(rows=0) == L.MSGL_INVALID_ARG
+    assert call(start=-1) == L.MSGL_INVALID_ARG
+    assert call(T=-1) == L.MSGL_INVALID_ARG
+    assert call(ids=None) == L.MSGL_INVALID_ARG and "NULL" in L.msgl_last_error()
+    assert call(out=None) == L.MSGL_INVALID_ARG
+    assert call(None, None, ids=None, T=0) == L.MSGL_OK
+
+
 def test_rope_store_kv_argument_checks(L):
     lib = L.lib
 
