@@ -244,6 +244,48 @@ def _time_stream(fn, stream, iters, warm=3):
     return a.elapsed_time(b) / iters
 
 
+def shared_prefix_leg(iters: int, stream) -> dict:
+    """Cascade decode (msgl_decode_attn_shared_prefix) and plain decode attention
+    on one decode batch whose requests share radix prefixes.  Unique bytes count
+    each shared prefix's K/V rows once per group, everything else as decode."""
+    import torch
+
+    from paged_kv_attention_slots_amd import _lib, runner, workloads as wl
+
+    sp = wl.shared_prefix_decode(device=stream.device)
+    w = sp.w
+    out = torch.empty_like(w.q)
+    lse = torch.empty(w.bs, w.q_heads, dtype=torch.float32, device=w.q.device)
+    ws = _lib.shared_prefix_workspace(w.bs, w.q_heads, w.head_dim, w.max_seq_len, device=w.q.device)
+    ws_d = _lib.decode_workspace(w.bs, w.q_heads, w.head_dim, w.max_seq_len, device=w.q.device)
+
+    def cascade():
+        _lib.msgl_decode_attn_shared_prefix(out, lse, w.q, w.k_pool, w.v_pool, w.page_table, w.table_idx,
+                                            w.seq_lens, sp.group_start, sp.prefix_lens, sp.max_group_size,
+                                            sp.max_prefix_len, w.max_seq_len, ws, page_size=w.page_size,
+                                            stream=stream)
+
+    def plain():
+        runner.decode_attn(w, w.k_pool, w.v_pool, out=out, lse=lse, workspace=ws_d, stream=stream)
+
+    c_ms = _time_stream(cascade, stream, iters)
+    p_ms = _time_stream(plain, stream, iters)
+    e = w.dtype.itemsize
+    row = w.kv_heads * w.head_dim * 2 * e  # K and V of one token
+    gs = sp.group_start.cpu().tolist()
+    shared_tok = sum(int(sp.prefix_lens[gs[g]]) for g in range(len(gs) - 1))
+    own_tok = int((w.seq_lens - sp.prefix_lens).long().sum())
+    qo = 2 * w.bs * w.q_heads * w.head_dim * e
+    unique = (shared_tok + own_tok) * (row + 4) + qo
+    plain_bytes = decode_bytes(w)
+    return {"batch": w.bs, "groups": len(gs) - 1, "shared_prefix_tokens": shared_tok,
+            "context_tokens": int(w.seq_lens.sum()), "cascade_ms": round(c_ms, 4), "plain_decode_ms": round(p_ms, 4),
+            "speedup": round(p_ms / c_ms, 2), "cascade_unique_GBs": round(unique / (c_ms * 1e-3) / 1e9, 1),
+            "cascade_frac_hbm": round(unique / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "plain_GBs": round(plain_bytes / (p_ms * 1e-3) / 1e9, 1), "unique_bytes": unique,
+            "plain_bytes": plain_bytes}
+
+
 def sweep(iters: int) -> int:
     """Secondary measurements (one JSON line each): the captured decode step at
     every padded batch size for page sizes 1 and 16, padding runs, eager
@@ -536,6 +578,11 @@ def main() -> int:
                       "frac_hbm": round(vbytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": vbytes}
         del vb, e_out
 
+    # decode over shared radix prefixes (4 groups of 64 requests on 4096-token
+    # prefixes, Qwen3-8B heads): the cascade call against plain decode attention
+    log("building the shared-prefix decode batch and timing it")
+    cascade = shared_prefix_leg(args.kernel_iters, stream)
+
     dbytes = decode_bytes(w4)
     sbytes = store_bytes(w4)
     flops3 = prefill_flops(w3)
@@ -607,6 +654,7 @@ def main() -> int:
         "prefill_attn_frac_of_bf16_peak": round(pattn_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
         "rope_store_kv": rope,
         "vocab_embed": vocab,
+        "shared_prefix_decode": cascade,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode attention (split + merge), eager, bs 256",

@@ -13,7 +13,8 @@
  * Conventions shared by every call
  * --------------------------------
  * Pointers named *_pool, q, q_out, out, lse, k_new, v_new, page_table, table_idx,
- * seq_lens, cached_lens, cu_q, positions, out_loc, weight, ids and workspace are DEVICE pointers owned
+ * seq_lens, cached_lens, cu_q, positions, out_loc, weight, ids, group_start,
+ * prefix_lens and workspace are DEVICE pointers owned
  * by the caller; the library never frees or retains them (except a captured
  * graph, which records them; see msgl_decode_graph_create).  `stream` is a
  * hipStream_t passed as void* (NULL = the null stream).  Calls only enqueue
@@ -164,6 +165,45 @@ msgl_status msgl_decode_attn(void *out, float *lse, const void *q, const void *k
                              void *stream);
 
 /*
+ * Cascade decode over shared radix prefixes.  The requests of a group (batch
+ * rows group_start[g] .. group_start[g+1]-1, consecutive) share the first
+ * prefix_lens[b] keys of their page-table rows: the same slot ids, as the
+ * radix prefix cache hands them out (Mini-SGLang's RadixPrefixCache; "Stage 4
+ * milestone", table 'What each chapter adds').  The result is exactly the
+ * decode attention of msgl_decode_attn (same out and lse, within float32
+ * rounding); the shared keys' K/V rows are read once per group instead of
+ * once per request.  The group's queries meet the shared keys on matrix cores
+ * (split along the keys to fill the GPU); each request's own keys
+ * prefix_lens[b] .. seq_lens[b]-1 go through the split-K decode; the partial
+ * results are merged by the log-sum-exp rule.
+ *
+ * group_start [num_groups + 1] and prefix_lens [batch] are device arrays.
+ * Preconditions (msgl_validate_shared_prefix checks host copies):
+ * group_start[0] == 0, groups non-empty and increasing, at most
+ * max_group_size requests each; prefix_lens equal within a group, in
+ * [0, min(seq_len - 1, max_prefix_len)] (the new token is never shared), and
+ * 0 for a request in no group; page-table entries 0 .. prefix_len-1 equal
+ * across a group's rows.  num_groups <= min(batch, 1024); 0 <= max_prefix_len
+ * < max_seq_len.  Other arguments as for msgl_decode_attn.  bf16 with
+ * head_dim 128 only (else MSGL_UNSUPPORTED).  The workspace holds the decode
+ * workspace plus float32 partial results; size it with
+ * msgl_decode_shared_prefix_workspace_bytes.
+ */
+size_t msgl_decode_shared_prefix_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim,
+                                                 int32_t max_seq_len, int32_t chunk);
+
+msgl_status msgl_decode_attn_shared_prefix(void *out, float *lse, const void *q, const void *k_pool,
+                                           const void *v_pool, int64_t num_slots, const int32_t *page_table,
+                                           int32_t row_stride, const int32_t *table_idx,
+                                           const int32_t *seq_lens, int32_t batch,
+                                           const int32_t *group_start, const int32_t *prefix_lens,
+                                           int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len,
+                                           int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                           int32_t page_size, int32_t max_seq_len, int32_t chunk,
+                                           float sm_scale, msgl_dtype dtype, void *workspace,
+                                           size_t workspace_bytes, void *stream);
+
+/*
  * Prefill / extend attention over a cached prefix (ragged batch).
  * Request b has seq_lens[b] tokens of which the first cached_lens[b] are
  * already in the pool from earlier steps; its new tokens are q rows
@@ -234,6 +274,17 @@ msgl_status msgl_validate_batch(const int32_t *page_table, int32_t rows, int32_t
                                 const int32_t *cached_lens, const int32_t *cu_q, int32_t batch,
                                 int32_t max_seq_len, int64_t num_slots, int32_t page_size,
                                 const int32_t *out_loc, int32_t num_tokens, int64_t dummy_slot);
+
+/*
+ * msgl_validate_shared_prefix - check the group metadata of
+ * msgl_decode_attn_shared_prefix on HOST copies (the preconditions listed
+ * there).  Returns MSGL_OK or MSGL_INVALID_ARG with the first violation in
+ * msgl_last_error.
+ */
+msgl_status msgl_validate_shared_prefix(const int32_t *page_table, int32_t rows, int32_t row_stride,
+                                        const int32_t *table_idx, const int32_t *seq_lens, int32_t batch,
+                                        const int32_t *group_start, const int32_t *prefix_lens,
+                                        int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len);
 
 #ifdef __cplusplus
 }

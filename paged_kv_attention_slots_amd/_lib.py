@@ -32,7 +32,8 @@ EXPORTS = (
     "msgl_last_error", "msgl_version", "msgl_store_kv", "msgl_rope_store_kv", "msgl_vocab_embed",
     "msgl_decode_workspace_bytes",
     "msgl_decode_attn", "msgl_prefill_attn", "msgl_decode_graph_create", "msgl_graph_launch",
-    "msgl_graph_destroy", "msgl_validate_batch",
+    "msgl_graph_destroy", "msgl_validate_batch", "msgl_decode_shared_prefix_workspace_bytes",
+    "msgl_decode_attn_shared_prefix", "msgl_validate_shared_prefix",
 )
 
 
@@ -63,6 +64,13 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msgl_decode_attn.restype = st
     lib.msgl_decode_attn.argtypes = [P, P, P, P, P, I64, P, I32, P, P, I32, I32, I32, I32, I32, I32,
                                      I32, F, st, P, SZ, P]
+    lib.msgl_decode_shared_prefix_workspace_bytes.restype = SZ
+    lib.msgl_decode_shared_prefix_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.msgl_decode_attn_shared_prefix.restype = st
+    lib.msgl_decode_attn_shared_prefix.argtypes = [P, P, P, P, P, I64, P, I32, P, P, I32, P, P, I32, I32, I32,
+                                                   I32, I32, I32, I32, I32, I32, F, st, P, SZ, P]
+    lib.msgl_validate_shared_prefix.restype = st
+    lib.msgl_validate_shared_prefix.argtypes = [P, I32, I32, P, P, I32, P, P, I32, I32, I32]
     lib.msgl_prefill_attn.restype = st
     lib.msgl_prefill_attn.argtypes = [P, P, P, P, P, I64, P, I32, P, P, P, P, I32, I32, I32, I32, I32,
                                       I32, I32, F, st, P]
@@ -176,6 +184,38 @@ def msgl_decode_attn(out, lse, q, k_pool, v_pool, page_table, table_idx, seq_len
                                 _p(_i32(page_table)), page_table.shape[1], _p(_i32(table_idx)),
                                 _p(_i32(seq_lens)), bs, H, G, d, page_size, max_seq_len, chunk,
                                 sm_scale, _dt(q), _p(workspace), workspace.numel(), _stream(stream)))
+
+
+def shared_prefix_workspace(batch: int, q_heads: int, head_dim: int, max_seq_len: int, chunk: int = 0,
+                            device="cuda") -> torch.Tensor:
+    """A workspace for msgl_decode_attn_shared_prefix (its contents need no initialisation)."""
+    n = int(lib.msgl_decode_shared_prefix_workspace_bytes(batch, q_heads, head_dim, max_seq_len, chunk))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def msgl_decode_attn_shared_prefix(out, lse, q, k_pool, v_pool, page_table, table_idx, seq_lens, group_start,
+                                   prefix_lens, max_group_size: int, max_prefix_len: int, max_seq_len: int,
+                                   workspace, page_size: int = 1, chunk: int = 0,
+                                   sm_scale: Optional[float] = None, stream=None) -> None:
+    bs, H, d = q.shape
+    S, G, _ = k_pool.shape
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    _check(lib.msgl_decode_attn_shared_prefix(
+        _p(out), _p(lse), _p(q), _p(k_pool), _p(v_pool), S, _p(_i32(page_table)), page_table.shape[1],
+        _p(_i32(table_idx)), _p(_i32(seq_lens)), bs, _p(_i32(group_start)), _p(_i32(prefix_lens)),
+        group_start.numel() - 1, max_group_size, max_prefix_len, H, G, d, page_size, max_seq_len, chunk, sm_scale,
+        _dt(q), _p(workspace), workspace.numel(), _stream(stream)))
+
+
+def msgl_validate_shared_prefix(page_table, table_idx, seq_lens, group_start, prefix_lens, max_group_size: int,
+                                max_prefix_len: int) -> None:
+    """Check shared-prefix group metadata on host (CPU) tensors; raises MsglError."""
+    c = lambda t: _p(_i32(t), device=False)
+    _check(lib.msgl_validate_shared_prefix(c(page_table), page_table.shape[0], page_table.shape[1],
+                                           c(table_idx), c(seq_lens), table_idx.numel(), c(group_start),
+                                           c(prefix_lens), group_start.numel() - 1, max_group_size,
+                                           max_prefix_len))
 
 
 def msgl_prefill_attn(out, lse, q, k_pool, v_pool, page_table, table_idx, seq_lens, cached_lens, cu_q,

@@ -112,6 +112,8 @@ msgl::DecodeArgs decode_args(void *out, float *lse, const void *q, const void *k
     const size_t pieces = (size_t)batch + msgl::kMaxDecodeGrid;
     a.part_o = reinterpret_cast<float *>(ws + msgl::kCtrlBytes + msgl::decode_prefix_bytes(batch));
     a.part_ml = a.part_o + pieces * q_heads * head_dim;
+    a.key_start = nullptr;
+    a.out_f32 = 0;
     return a;
 }
 
@@ -252,6 +254,57 @@ msgl_status msgl_decode_attn(void *out, float *lse, const void *q, const void *k
                     "decode launch");
 }
 
+size_t msgl_decode_shared_prefix_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim,
+                                                 int32_t max_seq_len, int32_t chunk) {
+    if (batch < 0 || q_heads < 1 || head_dim < 1 || max_seq_len < 1) return 0;
+    return msgl::shared_prefix_workspace_bytes(batch, q_heads, head_dim, max_seq_len, effective_chunk(chunk));
+}
+
+msgl_status msgl_decode_attn_shared_prefix(void *out, float *lse, const void *q, const void *k_pool,
+                                           const void *v_pool, int64_t num_slots, const int32_t *page_table,
+                                           int32_t row_stride, const int32_t *table_idx,
+                                           const int32_t *seq_lens, int32_t batch,
+                                           const int32_t *group_start, const int32_t *prefix_lens,
+                                           int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len,
+                                           int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                           int32_t page_size, int32_t max_seq_len, int32_t chunk,
+                                           float sm_scale, msgl_dtype dtype, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+    if (dtype != MSGL_BF16 || head_dim != 128)
+        return fail(MSGL_UNSUPPORTED, "the shared-prefix decode runs bf16 with head_dim 128 only");
+    const size_t need = msgl::shared_prefix_workspace_bytes(batch < 0 ? 0 : batch, q_heads < 1 ? 1 : q_heads,
+                                                            head_dim, max_seq_len, effective_chunk(chunk));
+    // the decode checks, against the decode part of the workspace
+    msgl_status s = check_decode(out, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx, seq_lens,
+                                 batch, q_heads, kv_heads, head_dim, page_size, max_seq_len, chunk, dtype,
+                                 workspace, workspace_bytes);
+    if (s != MSGL_OK) return s;
+    if (workspace_bytes < need)
+        return fail(MSGL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (num_groups < 0 || num_groups > batch)
+        return fail(MSGL_INVALID_ARG, "num_groups %d not in [0, batch=%d]", num_groups, batch);
+    if (num_groups > 1024) return fail(MSGL_UNSUPPORTED, "num_groups %d > 1024", num_groups);
+    if (max_prefix_len < 0 || max_prefix_len >= max_seq_len)
+        return fail(MSGL_INVALID_ARG, "max_prefix_len %d not in [0, max_seq_len)", max_prefix_len);
+    if (num_groups > 0 && (max_group_size < 1 || max_group_size > batch))
+        return fail(MSGL_INVALID_ARG, "max_group_size %d not in [1, batch=%d]", max_group_size, batch);
+    if (batch == 0) return ok();
+    if (!prefix_lens || (num_groups > 0 && !group_start)) return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    msgl::DecodeArgs d = decode_args(out, lse, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx,
+                                     seq_lens, batch, q_heads, kv_heads, head_dim, max_seq_len, chunk, sm_scale,
+                                     workspace);
+    msgl::SharedPrefixArgs sp;
+    sp.group_start = group_start;
+    sp.prefix_lens = prefix_lens;
+    sp.num_groups = num_groups;
+    sp.max_group_size = max_group_size;
+    sp.max_prefix_len = max_prefix_len;
+    sp.cus = msgl::device_cu_count();
+    sp.workspace = workspace;
+    return from_hip(msgl::launch_decode_shared_prefix(sp, d, head_dim, static_cast<hipStream_t>(stream)),
+                    "shared-prefix decode launch");
+}
+
 msgl_status msgl_prefill_attn(void *out, float *lse, const void *q, const void *k_pool,
                               const void *v_pool, int64_t num_slots, const int32_t *page_table,
                               int32_t row_stride, const int32_t *table_idx,
@@ -294,6 +347,9 @@ msgl_status msgl_prefill_attn(void *out, float *lse, const void *q, const void *
     a.q_heads = q_heads;
     a.kv_heads = kv_heads;
     a.scale_log2 = sm_scale * msgl::kLog2eHost;
+    a.splits = 1;
+    a.part_o = nullptr;
+    a.part_lse = nullptr;
     return from_hip(msgl::launch_prefill(a, static_cast<msgl::DType>(dtype), head_dim,
                                          static_cast<hipStream_t>(stream)),
                     "prefill launch");
@@ -367,6 +423,43 @@ void msgl_graph_destroy(msgl_graph *graph) {
     if (graph->exec) (void)hipGraphExecDestroy(graph->exec);
     if (graph->graph) (void)hipGraphDestroy(graph->graph);
     delete graph;
+}
+
+msgl_status msgl_validate_shared_prefix(const int32_t *page_table, int32_t rows, int32_t row_stride,
+                                        const int32_t *table_idx, const int32_t *seq_lens, int32_t batch,
+                                        const int32_t *group_start, const int32_t *prefix_lens,
+                                        int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len) {
+    if (!page_table || !table_idx || !seq_lens || !prefix_lens || (num_groups > 0 && !group_start))
+        return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    if (rows < 1 || row_stride < 1 || batch < 0 || num_groups < 0) return fail(MSGL_INVALID_ARG, "bad scalar argument");
+    std::vector<char> grouped((size_t)batch, 0);
+    if (num_groups > 0 && group_start[0] != 0) return fail(MSGL_INVALID_ARG, "group_start[0] = %d, expected 0", group_start[0]);
+    for (int32_t g = 0; g < num_groups; ++g) {
+        const int32_t b0 = group_start[g], b1 = group_start[g + 1];
+        if (b1 <= b0 || b1 > batch)
+            return fail(MSGL_INVALID_ARG, "group %d spans rows [%d, %d) of a batch of %d", g, b0, b1, batch);
+        if (b1 - b0 > max_group_size)
+            return fail(MSGL_INVALID_ARG, "group %d has %d requests > max_group_size %d", g, b1 - b0, max_group_size);
+        const int32_t P = prefix_lens[b0];
+        const int32_t *row0 = page_table + (int64_t)table_idx[b0] * row_stride;
+        for (int32_t b = b0; b < b1; ++b) {
+            grouped[(size_t)b] = 1;
+            if (table_idx[b] < 0 || table_idx[b] >= rows)
+                return fail(MSGL_INVALID_ARG, "table_idx[%d] = %d outside [0, %d)", b, table_idx[b], rows);
+            if (prefix_lens[b] != P)
+                return fail(MSGL_INVALID_ARG, "prefix_lens[%d] = %d differs from its group's %d", b, prefix_lens[b], P);
+            if (P < 0 || P > max_prefix_len || P >= seq_lens[b] || P > row_stride)
+                return fail(MSGL_INVALID_ARG, "prefix_lens[%d] = %d not in [0, min(seq_len - 1, max_prefix_len)]", b, P);
+            const int32_t *row = page_table + (int64_t)table_idx[b] * row_stride;
+            for (int32_t j = 0; j < P; ++j)
+                if (row[j] != row0[j])
+                    return fail(MSGL_INVALID_ARG, "request %d's page-table entry %d differs from its group's prefix", b, j);
+        }
+    }
+    for (int32_t b = 0; b < batch; ++b)
+        if (!grouped[(size_t)b] && prefix_lens[b] != 0)
+            return fail(MSGL_INVALID_ARG, "request %d is in no group but has prefix_lens %d (expected 0)", b, prefix_lens[b]);
+    return ok();
 }
 
 msgl_status msgl_validate_batch(const int32_t *page_table, int32_t rows, int32_t row_stride,

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
         if (lane == 0) s_tok[0] = 0;
         for (int base = 0; base < a.batch; base += 64) {
             const int b = base + lane;
-            int n = b < a.batch ? max(0, min(a.seq_lens[b], lmax)) : 0;
+            int n = b < a.batch ? max(0, min(a.seq_lens[b], lmax) - (a.key_start ? max(0, a.key_start[b]) : 0)) : 0;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const int y = __shfl_up(n, off);
@@ -97,7 +97,8 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
         const int je = (int)min((int64_t)L, (int64_t)j + (end - cur));
         if (je > j) {
             const int kvh = hg * wpb + wave;
-            const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride;
+            const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride +
+                                (a.key_start ? max(0, a.key_start[b]) : 0);
             QSlice<T> q[GQ];
             const T *qp = reinterpret_cast<const T *>(a.q) +
                           ((int64_t)b * a.q_heads + (int64_t)kvh * GQ) * D + lr * E;
@@ -119,9 +120,15 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
                         float f[E];
 #pragma unroll
                         for (int e = 0; e < E; ++e) f[e] = st.o[h][e] * inv;
-                        T *op = reinterpret_cast<T *>(a.out) + ((int64_t)b * a.q_heads + qh0 + h) * D +
-                                lr * E;
-                        st16(op, Store<T>::narrow(f));
+                        const int64_t oi = ((int64_t)b * a.q_heads + qh0 + h) * D + lr * E;
+                        if (a.out_f32) {
+#pragma unroll
+                            for (int e = 0; e < E; e += 4)
+                                *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + oi + e) =
+                                    make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+                        } else {
+                            st16(reinterpret_cast<T *>(a.out) + oi, Store<T>::narrow(f));
+                        }
                         if (a.lse != nullptr && lr == 0)
                             a.lse[(int64_t)b * a.q_heads + qh0 + h] = (st.m[h] + __log2f(st.l[h])) * kLn2;
                     }
@@ -189,7 +196,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     }
     const float inv = 1.0f / l;
     T *op = reinterpret_cast<T *>(a.out) + ((int64_t)b * a.q_heads + h) * D + lane * PER;
-    if constexpr (sizeof(T) == 2) {
+    if (a.out_f32) {
+        float *fo = static_cast<float *>(a.out) + ((int64_t)b * a.q_heads + h) * D + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) fo[e] = acc[e] * inv;
+    } else if constexpr (sizeof(T) == 2) {
         if constexpr (PER == 2) {
             *reinterpret_cast<uint32_t *>(op) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
         } else {
@@ -205,8 +216,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // host side
 
-namespace {
-
 int device_cu_count() {
     static int cached[64] = {0};
     int dev = 0;
@@ -219,6 +228,8 @@ int device_cu_count() {
     }
     return cached[dev];
 }
+
+namespace {
 
 // Loads per wave-iteration of the decode pipeline (4 tokens per load for
 // 256-byte head slices: 16 tokens per iteration).

@@ -19,6 +19,10 @@ constexpr size_t kCtrlBytes = 256;
 constexpr int kMaxDecodeGrid = 4096;
 
 inline size_t decode_prefix_bytes(int batch) { return ((size_t)(batch + 1) * 4 + 255) / 256 * 256; }
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Key splits of the shared-prefix pass (upper bound; sizes the workspace).
+constexpr int kMaxPrefixSplits = 16;
 
 struct StoreKvArgs {
     void *k_pool;
@@ -80,6 +84,8 @@ struct DecodeArgs {
     int32_t *prefix;      // [batch + 1] keys before each request (written by the split kernel)
     float *part_o;        // [batch + kMaxDecodeGrid, q_heads, head_dim]
     float *part_ml;       // [batch + kMaxDecodeGrid, q_heads, 2]  (max in log2 units, sum)
+    const int32_t *key_start;  // nullable: request b attends keys key_start[b] .. seq_lens[b]-1
+    int32_t out_f32;      // nonzero: out is float32 whatever the storage type
 };
 
 struct PrefillArgs {
@@ -101,9 +107,34 @@ struct PrefillArgs {
     int32_t q_heads;
     int32_t kv_heads;
     float scale_log2;
+    // shared-prefix mode only (prefill_mfma_kernel<GQ, true>): key splits per
+    // query block, and the partial outputs [splits, total_q, q_heads, head_dim]
+    // and lse [splits, total_q, q_heads] (float32, natural log)
+    int32_t splits;
+    float *part_o;
+    float *part_lse;
 };
 
 size_t decode_workspace_bytes(int batch, int q_heads, int head_dim, int max_seq_len, int chunk);
+
+// Cascade decode over shared radix prefixes (bf16, head_dim 128).
+struct SharedPrefixArgs {
+    const int32_t *group_start;  // [num_groups + 1] batch rows of each group
+    const int32_t *prefix_lens;  // [batch] shared prefix length of each request's group
+    int32_t num_groups;
+    int32_t max_group_size;
+    int32_t max_prefix_len;
+    int32_t cus;                 // compute units of the device (sizes the key split)
+    void *workspace;             // shared_prefix_workspace_bytes(...)
+};
+size_t shared_prefix_workspace_bytes(int batch, int q_heads, int head_dim, int max_seq_len, int chunk);
+int prefix_splits(int num_groups, int max_group_size, int max_prefix_len, int q_heads, int kv_heads, int cus);
+// dec: the decode arguments of the whole batch (out = the bf16 output, lse,
+// workspace = the start of the shared-prefix workspace); prepare_only as for
+// launch_decode.
+hipError_t launch_decode_shared_prefix(const SharedPrefixArgs &sp, const DecodeArgs &dec, int head_dim,
+                                       hipStream_t stream, bool prepare_only = false);
+int device_cu_count();
 
 hipError_t launch_store_kv(const StoreKvArgs &a, hipStream_t stream);
 hipError_t launch_rope_store_kv(const RopeStoreKvArgs &a, DType dtype, hipStream_t stream);
@@ -115,5 +146,8 @@ hipError_t launch_decode(const DecodeArgs &a, DType dtype, int head_dim, hipStre
 // bf16 prefill on matrix cores when the shape is supported, else the VALU path.
 hipError_t launch_prefill(const PrefillArgs &a, DType dtype, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_valu(const PrefillArgs &a, DType dtype, int head_dim, hipStream_t stream);
+// Shared-prefix pass of the cascade decode: bf16, head_dim 128 (a.splits,
+// a.part_o and a.part_lse set; a.batch = groups, a.cu_q = group offsets).
+hipError_t launch_prefill_shared(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace msgl

@@ -228,7 +228,12 @@ struct BlockItem {
 // from the lane that holds them.  Up to 4 requests per lane the first q row
 // and page-table row come in the same round trip as the lengths; beyond, they
 // are read once the request is known (registers are scarcer there).
-template <int BQ, int NB>
+//
+// Shared-prefix mode (SH): "request" b is a group of decode requests, rows
+// cu_q[b] .. cu_q[b+1]-1 of q, that share the first cached_lens[cu_q[b]]
+// keys of their page-table rows; its "new tokens" are the group's queries and
+// its cached tokens that shared prefix, read through the first member's row.
+template <int BQ, int NB, bool SH = false>
 MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
     constexpr bool kAll = NB <= 4;
     constexpr int NX = kAll ? NB : 1;
@@ -244,7 +249,17 @@ MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
             Q0[k % NX] = 0;
             TI[k % NX] = 0;
         }
-        if (b < a.batch) {
+        if (SH && b < a.batch) {
+            const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
+            if (q0 >= 0 && q1 > q0 && q1 <= a.total_q) {  // a malformed group gets no blocks
+                C[k] = (int)min((int64_t)a.cached_lens[q0], a.row_stride);
+                E[k] = C[k] <= 0 ? 0 : q1 - q0;
+                if (kAll) {
+                    Q0[k % NX] = q0;
+                    TI[k % NX] = a.table_idx[q0];
+                }
+            }
+        } else if (b < a.batch) {
             const int L = (int)min((int64_t)a.seq_lens[b], a.row_stride);
             C[k] = a.cached_lens[b];
             E[k] = C[k] < 0 ? 0 : L - C[k];
@@ -304,7 +319,11 @@ MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
             if constexpr (kAll)
                 return {b, __shfl(q0 + k - (incl - c), src), __shfl(E[j], src), __shfl(C[j], src),
                         __shfl(Q0[j % NX], src), __shfl(TI[j % NX], src)};
-            else
+            else if constexpr (SH) {
+                const int qr = a.cu_q[__builtin_amdgcn_readfirstlane(b)];
+                return {b, __shfl(q0 + k - (incl - c), src), __shfl(E[j], src), __shfl(C[j], src), qr,
+                        a.table_idx[qr]};
+            } else
                 return {b, __shfl(q0 + k - (incl - c), src), __shfl(E[j], src), __shfl(C[j], src),
                         a.cu_q[__builtin_amdgcn_readfirstlane(b)], a.table_idx[__builtin_amdgcn_readfirstlane(b)]};
         }
@@ -586,7 +605,13 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 // visible (K of t+1, V of t, issued in tile t-1, and the ids of t+2 for this
 // tile's gathers); then it refills the stages tile t-1 used, K of t+2 and V of
 // t+1, copies the ids of t+3, and runs units 2t and 2t+1 as above.
-template <int GQ>
+//
+// In shared-prefix mode (SH, decode requests grouped by a shared radix prefix)
+// the block id also carries a key split s < a.splits: the block attends its
+// group's queries to split s of the shared prefix (no causal mask: every
+// query sits after the prefix) and writes the normalised partial output and
+// its lse, in float32, to split s of the partial arrays.
+template <int GQ, bool SH = false>
 __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
     constexpr int BQ = pfc::kCols / GQ;  // query tokens per block
     __shared__ __attribute__((aligned(1024))) char smem[pfc::kLds];
@@ -597,11 +622,14 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int jj = lane >> 5;
     const int G = a.kv_heads;
 
-    // block id = list entry * G + kv head: the query blocks longest first, no gaps
-    const int kvh = blockIdx.x % G;
-    const BlockItem item = a.batch <= 64    ? sorted_block<BQ, 1>(a, blockIdx.x / G, lane)
-                           : a.batch <= 256 ? sorted_block<BQ, 4>(a, blockIdx.x / G, lane)
-                                            : sorted_block<BQ, pf::kMaxBatch / 64>(a, blockIdx.x / G, lane);
+    // block id = (list entry * G + kv head) [* splits + split]: the query blocks
+    // longest first, no gaps
+    const int split = SH ? (int)(blockIdx.x % a.splits) : 0;
+    const int bid = SH ? (int)(blockIdx.x / a.splits) : (int)blockIdx.x;
+    const int kvh = bid % G;
+    const BlockItem item = a.batch <= 64    ? sorted_block<BQ, 1, SH>(a, bid / G, lane)
+                           : a.batch <= 256 ? sorted_block<BQ, 4, SH>(a, bid / G, lane)
+                                            : sorted_block<BQ, pf::kMaxBatch / 64, SH>(a, bid / G, lane);
     const int b = __builtin_amdgcn_readfirstlane(item.b);
     const int qb = __builtin_amdgcn_readfirstlane(item.qb);
     if (b < 0) return;  // past the last query block: uniform over the block, before any barrier
@@ -611,9 +639,12 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     if (qb < 0 || C < 0 || t0 >= E) return;
     const int row0 = __builtin_amdgcn_readfirstlane(item.q0) + t0;
     const int ntok = min(min(BQ, E - t0), a.total_q - row0);
-    if (ntok <= 0) return;
-    const int pos0 = C + t0;         // position of the block's first token
-    const int nkeys = pos0 + ntok;   // keys 0 .. position of its last token
+    if (ntok <= 0 || row0 < 0) return;
+    // SH: keys k0 .. k0 + span - 1 of the shared prefix (splits of whole tiles)
+    const int span = SH ? (((C + a.splits - 1) / a.splits + pf::kKT - 1) / pf::kKT) * pf::kKT : 0;
+    const int k0 = SH ? min(C, split * span) : 0;
+    const int pos0 = SH ? min(C, k0 + span) - k0 - 1 : C + t0;  // SH: every query sees the whole split
+    const int nkeys = SH ? pos0 + 1 : pos0 + ntok;  // keys 0 .. position of its last token
     const int ntiles = (nkeys + pf::kKT - 1) / pf::kKT;
 
     // this lane's query column
@@ -622,13 +653,21 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int hq = kvh * GQ + col % GQ;
     const bool valid = tl < ntok;
     const int tok = valid ? tl : ntok - 1;
-    const int pos = pos0 + tok;
+    const int pos = SH ? pos0 : pos0 + tok;
+
+    if constexpr (SH) {
+        if (nkeys <= 0) {  // an empty split: an empty softmax state, marked by lse = -inf
+            if (valid && jj == 0)
+                a.part_lse[((int64_t)split * a.total_q + row0 + tl) * a.q_heads + hq] = -INFINITY;
+            return;
+        }
+    }
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)smem;
     // page-table ids: each wave copies all 64 ids of a tile into its own slot
     // (keys past the block's last one read key 0's id: a real row whose scores
     // the causal mask removes)
-    const int32_t *pt = a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(item.row) * a.row_stride;
+    const int32_t *pt = a.page_table + (int64_t)__builtin_amdgcn_readfirstlane(item.row) * a.row_stride + k0;
     const uint32_t ids_wave = lds0 + pfc::kIdsBase + wave * pf::kIdSlots * pf::kKT * 4;
     auto copy_ids = [&](int t) __attribute__((always_inline)) {
         const int key = t * pf::kKT + lane;
@@ -827,6 +866,22 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     unit(2 * ntiles - 1, last, 0, false, false);
 
     lt = add_with_other_half(lt);
+    if constexpr (SH) {
+        if (valid) {
+            const float inv = 1.0f / lt;
+            const int64_t r = ((int64_t)split * a.total_q + row0 + tl) * a.q_heads + hq;
+            float *op = a.part_o + r * pf::kD;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<float4 *>(op + db * 32 + 8 * i + 4 * jj) =
+                        make_float4(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv, acc[db][4 * i + 2] * inv,
+                                    acc[db][4 * i + 3] * inv);
+            if (jj == 0) a.part_lse[r] = (m + __log2f(lt)) * kLn2;
+        }
+        return;
+    }
     if (valid) {
         const float inv = 1.0f / lt;
         bf16_t *op = reinterpret_cast<bf16_t *>(a.out) + ((int64_t)(row0 + tl) * a.q_heads + hq) * pf::kD;
@@ -871,6 +926,23 @@ hipError_t run_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_prefill_shared(const PrefillArgs &a, hipStream_t stream) {
+    if (a.batch > pf::kMaxBatch || a.splits < 1) return hipErrorInvalidValue;
+    const int g = a.q_heads / a.kv_heads;
+    const int BQ = pfc::kCols / g;
+    const int64_t grid = prefill_blocks(a, BQ) * a.splits;
+    if (grid < 1) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    switch (g) {
+        case 1: hipLaunchKernelGGL((prefill_mfma_kernel<1, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((prefill_mfma_kernel<2, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((prefill_mfma_kernel<4, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((prefill_mfma_kernel<8, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill(const PrefillArgs &a, DType dtype, int head_dim, hipStream_t stream) {
     if (dtype == kBF16 && head_dim == pf::kD && a.batch <= pf::kMaxBatch) {

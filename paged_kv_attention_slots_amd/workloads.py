@@ -681,3 +681,86 @@ def vocab_batch(seed: int = 1006, device="cpu", num_tokens: int = 4288, vocab: i
     lo, hi = vocab * rank // shards, vocab * (rank + 1) // shards
     weight = gen_rows(seed, STREAM_EMBED, torch.arange(lo, hi, dtype=torch.int64), hidden, std, dtype, device)
     return VocabBatch(f"vocab-{vocab}x{hidden}-tp{shards}r{rank}", weight, lo, vocab, ids)
+
+
+# ----------------------------------------------------------------------------
+# decode over shared radix prefixes
+# ----------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class SharedPrefixBatch:
+    w: Workload                # the decode batch (every request's full page-table row)
+    group_start: torch.Tensor  # int32 [groups + 1] batch rows of each group
+    prefix_lens: torch.Tensor  # int32 [bs] shared prefix length of each request's group (0: none)
+    max_group_size: int
+    max_prefix_len: int
+
+
+def shared_prefix_decode(seed: int = 1007, device="cpu", group_sizes=(64, 64, 64, 64),
+                         prefixes=(4096, 4096, 4096, 4096), singles: int = 0, suffix_lo: int = 16,
+                         suffix_hi: int = 1024, page_size: int = 1, num_slots: int = 1 << 20,
+                         heads=QWEN3_8B, q_std: Optional[float] = None,
+                         dtype: torch.dtype = torch.bfloat16) -> SharedPrefixBatch:
+    """Decode batch whose requests come in groups that share a radix prefix:
+    group g's requests hold the same slots for positions 0 .. prefixes[g]-1
+    (taken once from the shuffled free list, or as whole free pages at
+    page_size > 1, when the prefixes are page multiples), then their own
+    suffix of U[suffix_lo, suffix_hi] tokens, the last of which is the step's
+    new token.  `singles` more requests share nothing (prefix 0).  Defaults:
+    Qwen3-8B heads, bf16, batch 256 in 4 groups of 64 on 4096-token prefixes.
+    A shared slot's K/V values are those its group's last request writes."""
+    assert len(group_sizes) == len(prefixes)
+    rng = np.random.default_rng(seed)
+    n_grouped = int(sum(group_sizes))
+    bs = n_grouped + singles
+    suffix = rng.integers(suffix_lo, suffix_hi, size=bs, endpoint=True)
+    plen = np.zeros(bs, dtype=np.int64)
+    gstart = [0]
+    for n, P in zip(group_sizes, prefixes):
+        plen[gstart[-1]:gstart[-1] + n] = P
+        gstart.append(gstart[-1] + n)
+    lens = plen + suffix
+    rows = []
+    if page_size == 1:
+        free = rng.permutation(num_slots)
+        pos = 0
+        for g, (n, P) in enumerate(zip(group_sizes, prefixes)):
+            shared = free[pos:pos + P]
+            pos += P
+            for b in range(gstart[g], gstart[g] + n):
+                rows.append(np.concatenate([shared, free[pos:pos + suffix[b]]]))
+                pos += int(suffix[b])
+        for b in range(n_grouped, bs):
+            rows.append(free[pos:pos + suffix[b]])
+            pos += int(suffix[b])
+        assert pos <= num_slots, "pool too small for the batch"
+    else:
+        assert all(P % page_size == 0 for P in prefixes), "shared prefixes are whole pages"
+        free_pages = rng.permutation(num_slots // page_size)
+        pos = 0
+
+        def take(n_tok):
+            nonlocal pos
+            n = (n_tok + page_size - 1) // page_size
+            pages = free_pages[pos:pos + n].astype(np.int64)
+            pos += n
+            j = np.arange(n_tok)
+            return pages[j // page_size] * page_size + j % page_size
+
+        for g, (n, P) in enumerate(zip(group_sizes, prefixes)):
+            shared = take(P)
+            for b in range(gstart[g], gstart[g] + n):
+                rows.append(np.concatenate([shared, take(int(suffix[b]))]))
+        for b in range(n_grouped, bs):
+            rows.append(take(int(suffix[b])))
+        assert pos <= free_pages.size, "pool too small for the batch"
+    cached = [int(L) - 1 for L in lens]
+    max_len = int(lens.max())
+    w = build_workload(f"shared-prefix-decode-ps{page_size}", "decode", dtype, **heads, page_size=page_size,
+                       num_slots=num_slots, max_running_req=bs, max_seq_len=align_up_32(max_len + 1),
+                       rows=rows, seq_lens=lens, cached_lens=cached, seed=seed, kv_std=1.0,
+                       q_std=q_std if q_std is not None else 1.0 / math.sqrt(128), device=device)
+    return SharedPrefixBatch(w, torch.tensor(gstart, dtype=torch.int32, device=device),
+                             torch.from_numpy(plen.astype(np.int32)).to(device),
+                             max(group_sizes) if group_sizes else 1, max(prefixes) if prefixes else 0)

@@ -157,3 +157,64 @@ def test_lognormal_lengths():
     L = wl.lognormal_lengths(rng, 200000)
     assert L.min() >= 16 and L.max() <= 32768
     assert abs(np.median(L) - 2048) / 2048 < 0.02
+
+
+# --------------------------------------------------------------------------
+# shared radix prefixes: generator structure and the host validator
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("page_size", [1, 16])
+def test_shared_prefix_batch_structure(page_size):
+    from paged_kv_attention_slots_amd import _lib as L
+
+    sp = wl.shared_prefix_decode(group_sizes=(3, 2, 1), prefixes=(48, 16, 32), singles=2, suffix_hi=50,
+                                 num_slots=4096, page_size=page_size)
+    w = sp.w
+    assert sp.group_start.tolist() == [0, 3, 5, 6]
+    assert sp.prefix_lens.tolist() == [48, 48, 48, 16, 16, 32, 0, 0]
+    pt = w.page_table
+    for g in range(3):
+        b0, b1 = int(sp.group_start[g]), int(sp.group_start[g + 1])
+        P = int(sp.prefix_lens[b0])
+        for b in range(b0, b1):
+            assert torch.equal(pt[int(w.table_idx[b]), :P], pt[int(w.table_idx[b0]), :P])
+    # slots outside the shared prefixes are used once
+    used = torch.cat([pt[int(w.table_idx[b]), int(sp.prefix_lens[b]):int(w.seq_lens[b])] for b in range(w.bs)])
+    assert used.unique().numel() == used.numel()
+    L.msgl_validate_shared_prefix(pt, w.table_idx, w.seq_lens, sp.group_start, sp.prefix_lens, sp.max_group_size,
+                                  sp.max_prefix_len)
+    L.msgl_validate_batch(pt, w.table_idx, w.seq_lens, w.cached_lens, w.cu_q, max_seq_len=w.max_seq_len,
+                          num_slots=w.num_slots, page_size=page_size, out_loc=w.out_loc, dummy_slot=w.dummy_slot)
+
+
+def test_shared_prefix_validator_rejects():
+    from paged_kv_attention_slots_amd import _lib as L
+
+    sp = wl.shared_prefix_decode(group_sizes=(3, 2), prefixes=(48, 16), singles=1, suffix_hi=50, num_slots=4096)
+    w = sp.w
+    args = dict(max_group_size=sp.max_group_size, max_prefix_len=sp.max_prefix_len)
+
+    def bad(pt=w.page_table, seq=w.seq_lens, gs=sp.group_start, pl=sp.prefix_lens, **kw):
+        a = {**args, **kw}
+        with pytest.raises(L.MsglError) as e:
+            L.msgl_validate_shared_prefix(pt, w.table_idx, seq, gs, pl, a["max_group_size"], a["max_prefix_len"])
+        return str(e.value)
+
+    pt = w.page_table.clone()
+    pt[int(w.table_idx[1]), 7] += 1
+    assert "differs from its group's prefix" in bad(pt=pt)
+    pl = sp.prefix_lens.clone()
+    pl[2] = 40
+    assert "differs from its group" in bad(pl=pl)
+    seq = w.seq_lens.clone()
+    seq[0] = 48  # the prefix would hold the new token
+    assert "not in [0" in bad(seq=seq)
+    gs = sp.group_start.clone()
+    gs[0] = 1
+    assert "group_start[0]" in bad(gs=gs)
+    assert "max_group_size" in bad(max_group_size=2)
+    assert "not in [0" in bad(max_prefix_len=20)
+    pl = sp.prefix_lens.clone()
+    pl[5] = 3  # the single request is in no group
+    assert "in no group" in bad(pl=pl)
