@@ -133,7 +133,8 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes,
     lines = ["# rocprofv3 --kernel-trace --stats summary of the benchmark command",
              f"# command: rocprofv3 --kernel-trace --stats --output-format csv -- {command}",
              "# workload: Qwen3-8B decode bs 256 page_size 1 (graph + eager decode-attention launches),",
-             "#           ragged prefill 8 requests (Qwen3-0.6B heads); durations in microseconds", ""]
+             "#           ragged prefill 8 requests (Qwen3-0.6B heads), then the fused RoPE, vocabulary",
+             "#           indexing and shared-prefix legs; durations in microseconds", ""]
     head = f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_%':>8}  kernel"
     mine = [r for r in stats if "msgl::" in r["Name"]]
     other = [r for r in stats if "msgl::" not in r["Name"]]
@@ -142,17 +143,40 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes,
         name = r["Name"].replace('"', "")
         return (f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
                 f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}  {name[:110]}")
-    lines += ["## library kernels", head] + [row(r) for r in mine]
+
+    # per leg, from the trace: the decode / prefill step legs come before the
+    # first fused-RoPE launch; the RoPE, vocabulary and shared-prefix legs after
+    trace = _read_csv(_find(stats_dir, "kernel_trace.csv"))
+    cut = min([int(r["Dispatch_Id"]) for r in trace if "rope_store_kv_kernel" in r["Kernel_Name"]] or [1 << 62])
+
+    def legs(before):
+        per = {}
+        for r in trace:
+            if "msgl::" in r["Kernel_Name"] and (int(r["Dispatch_Id"]) < cut) == before:
+                per.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        out = []
+        for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"{len(d):6d} {sum(d) / len(d):10.2f} {min(d):10.2f} {max(d):10.2f} {'':>8}  {name[:110]}")
+        return out
+    lines += ["## library kernels, whole run", head] + [row(r) for r in mine]
+    lines += ["", "## the decode step (Qwen3-8B bs 256: graph replays, then eager launches) and the ragged prefill",
+              head] + legs(True)
+    lines += ["", "## after them: fused RoPE (decode and prefill batches), vocabulary indexing (4288 and 256 tokens),",
+              "## shared-prefix batch (cascade call: prefix MFMA pass, suffix decode, merge; then plain decode)",
+              head] + legs(False)
     lines += ["", "## largest other kernels (seeded input generation, torch copies)", head]
     lines += [row(r) for r in other[:6]]
     with open(os.path.join(PROFILE_DIR, "step_qwen3_8b_decode_bs256_ragged_prefill_kernel_stats.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
     def per_dispatch(dirname, counter):
+        # only the dispatches before the first fused-RoPE launch: the decode
+        # kernels after it belong to the shared-prefix leg's batch
         rows = _read_csv(_find(dirname, "counter_collection.csv"))
+        cut = min([int(r["Dispatch_Id"]) for r in rows if "rope_store_kv_kernel" in r["Kernel_Name"]] or [1 << 62])
         out = {}
         for r in rows:
-            if r["Counter_Name"] != counter:
+            if r["Counter_Name"] != counter or ("neg_kernel" not in r["Kernel_Name"] and int(r["Dispatch_Id"]) > cut):
                 continue
             out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)  # KiB -> B
         return out
@@ -180,7 +204,8 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes,
         "# HBM traffic of one decode-attention launch (split + merge kernels), Qwen3-8B shape, bs 256",
         f"# command (three runs): rocprofv3 --kernel-trace --stats | --pmc FETCH_SIZE | --pmc WRITE_SIZE "
         f"-- {command}",
-        "# counters are per dispatch (KiB), averaged over the eager launches; each is scaled by",
+        "# counters are per dispatch (KiB), averaged over the launches on this batch (the graph replays",
+        "# and the eager launches, all before the bench's fused-RoPE leg); each is scaled by",
         "# (known bytes / counter reading) of a plain copy kernel: torch.neg over 1 GiB of fp32",
         f"copy_fetch_scale = {f_scale:.4f}",
         f"copy_write_scale = {w_scale:.4f}",
