@@ -810,7 +810,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
             weights(sc, mn, pb_new, lt_u);
             asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u));
         }
-        if (has_scores && has_softmax) interleave_unit<1, 5, 2, 8>();
+        if (has_scores && has_softmax) interleave_unit<1, 4, 2, 8>();
         if (has_softmax && __any(mn != m)) {
             const float alpha = fast_exp2(m - mn);
             lt *= alpha;
