@@ -161,14 +161,33 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
+MSGL_DEV float wave_max64(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+MSGL_DEV float wave_sum64(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
 // Combine the pieces of every request that straddles block boundaries.
-// One wave per (request, q head); each lane owns D / 64 output elements.
+// One wave per (request, q head).  The pieces' (max, sum) states are read
+// lanes-over-pieces, 64 at a time, so a long request costs a few round trips
+// rather than one per piece.  For the outputs the wave splits into four
+// groups of 16 lanes; each lane owns D / 16 consecutive elements, group g
+// takes pieces g, g + 4, ..., and the groups' sums are added by lane exchange
+// at the end, so four pieces' loads are in flight per group.
 template <typename T, int D, int GQ>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-    constexpr int PER = D / 64;
+    constexpr int DPL = D / 16;  // elements per lane (a multiple of 4)
     const int b = blockIdx.x;
     const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4;
+    const int col = (lane & 15) * DPL;
     if (h >= a.q_heads) return;
     const int64_t total = a.ctrl[0];
     const int64_t share = a.ctrl[1];
@@ -179,36 +198,69 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     const int first = (int)(first_tok / share);
     const int last = (int)((first_tok + L - 1) / share);
     if (first == last) return;  // one piece: the split kernel wrote the output
+    const int n = last - first + 1;
+    // piece k of this request (block first + k) keeps its state at index (b + first + k) * q_heads + h
+    const int64_t i0 = ((int64_t)b + first) * a.q_heads + h;
+    const int64_t pstride = (int64_t)a.q_heads * D;  // floats between consecutive pieces' outputs
     float mx = -INFINITY;
-    for (int j = first; j <= last; ++j) mx = fmaxf(mx, a.part_ml[(((int64_t)b + j) * a.q_heads + h) * 2]);
+    for (int k = lane; k < n; k += 64) mx = fmaxf(mx, a.part_ml[(i0 + (int64_t)k * a.q_heads) * 2]);
+    mx = wave_max64(mx);
     float l = 0.0f;
-    float acc[PER];
+    float acc[DPL];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-#pragma unroll 4
-    for (int j = first; j <= last; ++j) {
-        const int64_t idx = ((int64_t)b + j) * a.q_heads + h;
-        const float w = fast_exp2(a.part_ml[idx * 2] - mx);
-        l = fmaf(a.part_ml[idx * 2 + 1], w, l);
-        const float *po = a.part_o + idx * D + lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(po[e], w, acc[e]);
-    }
-    const float inv = 1.0f / l;
-    T *op = reinterpret_cast<T *>(a.out) + ((int64_t)b * a.q_heads + h) * D + lane * PER;
-    if (a.out_f32) {
-        float *fo = static_cast<float *>(a.out) + ((int64_t)b * a.q_heads + h) * D + lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) fo[e] = acc[e] * inv;
-    } else if constexpr (sizeof(T) == 2) {
-        if constexpr (PER == 2) {
-            *reinterpret_cast<uint32_t *>(op) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-        } else {
-            *reinterpret_cast<uint16_t *>(op) = (uint16_t)f32_to_bf16_bits(acc[0] * inv);
+    for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+        const int k = c0 + lane;
+        float wk = 0.0f;
+        if (k < n) {
+            const int64_t idx = i0 + (int64_t)k * a.q_heads;
+            wk = fast_exp2(a.part_ml[idx * 2] - mx);
+            l = fmaf(a.part_ml[idx * 2 + 1], wk, l);
         }
+        const int cn = min(64, n - c0);
+        const float *po = a.part_o + i0 * D + (int64_t)c0 * pstride + col;
+#pragma unroll 4
+        for (int t0 = 0; t0 < cn; t0 += 4) {
+            const int t = t0 + grp;
+            const float w = __shfl(wk, t & 63);  // every lane takes part; past the end w is unused
+            if (t < cn) {
+                const float *pp = po + (int64_t)t * pstride;
+#pragma unroll
+                for (int e = 0; e < DPL; e += 4) {
+                    const float4 v = *reinterpret_cast<const float4 *>(pp + e);
+                    acc[e] = fmaf(v.x, w, acc[e]);
+                    acc[e + 1] = fmaf(v.y, w, acc[e + 1]);
+                    acc[e + 2] = fmaf(v.z, w, acc[e + 2]);
+                    acc[e + 3] = fmaf(v.w, w, acc[e + 3]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+        acc[e] += __shfl_xor(acc[e], 16);
+        acc[e] += __shfl_xor(acc[e], 32);
+    }
+    l = wave_sum64(l);
+    if (grp != 0) return;
+    const float inv = 1.0f / l;
+    const int64_t oi = ((int64_t)b * a.q_heads + h) * D + col;
+    if (a.out_f32) {
+        float *fo = static_cast<float *>(a.out) + oi;
+#pragma unroll
+        for (int e = 0; e < DPL; e += 4)
+            *reinterpret_cast<float4 *>(fo + e) =
+                make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+    } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < DPL; e += 4)
+            *reinterpret_cast<uint2 *>(reinterpret_cast<T *>(a.out) + oi + e) =
+                make_uint2(pack_bf16x2(acc[e] * inv, acc[e + 1] * inv), pack_bf16x2(acc[e + 2] * inv, acc[e + 3] * inv));
     } else {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) reinterpret_cast<float *>(op)[e] = acc[e] * inv;
+        for (int e = 0; e < DPL; e += 4)
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + oi + e) =
+                make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
     }
     if (a.lse != nullptr && lane == 0) a.lse[(int64_t)b * a.q_heads + h] = (mx + __log2f(l)) * kLn2;
 }
