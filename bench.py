@@ -360,7 +360,7 @@ def sweep(iters: int) -> int:
     for name, w in cases:
         out = torch.empty_like(w.q)
         ms = _time_stream(lambda: runner.prefill_attn(w, w.k_pool, w.v_pool, out=out, with_lse=False,
-                                                      stream=stream), stream, iters)
+                                                      stream=stream), stream, iters, warm=PREFILL_WARM_LAUNCHES)
         fl = prefill_flops(w)
         print(json.dumps({"sweep": "prefill_attn", "case": name, "tokens": w.num_tokens,
                           "context_tokens": int(w.seq_lens.sum()), "ms": round(ms, 4),
