@@ -312,6 +312,32 @@ def shared_prefix_leg(iters: int, stream) -> dict:
             "plain_bytes": plain_bytes}
 
 
+def flushed_timing(fn, stream, iters: int, flush_bytes: int = 1 << 30, warm: int = 3) -> dict:
+    """Per-launch times of ``fn`` with a write of ``flush_bytes`` to a scratch
+    buffer before each launch (outside the events), so the last-level cache
+    holds none of the kernel's inputs: median, p10 and p90 in ms."""
+    import torch
+
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device=stream.device)
+    for _ in range(warm):
+        fn()
+    times = []
+    for _ in range(iters):
+        with torch.cuda.stream(stream):
+            scratch.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del scratch
+    times.sort()
+    q = lambda f: times[min(len(times) - 1, int(f * (len(times) - 1) + 0.5))]
+    return {"median_ms": round(q(0.5), 4), "p10_ms": round(q(0.1), 4), "p90_ms": round(q(0.9), 4),
+            "iters": iters, "flush_bytes": flush_bytes}
+
+
 def sweep(iters: int) -> int:
     """Secondary measurements (one JSON line each): the captured decode step at
     every padded batch size for page sizes 1 and 16, padding runs, eager
@@ -612,6 +638,15 @@ def main() -> int:
     log("building the shared-prefix decode batch and timing it")
     cascade = shared_prefix_leg(args.kernel_iters, stream)
 
+    # both attention kernels again, one launch at a time after a 1 GiB cache flush
+    log("timing flushed launches (1 GiB written between launches)")
+    dflush = flushed_timing(lambda: runner.decode_attn(w4, k_pool4, v_pool4, out=out4, lse=lse4, workspace=ws4,
+                                                       chunk=args.chunk, stream=stream), stream, 30)
+    dflush["GBs"] = round(decode_bytes(w4) / (dflush["median_ms"] * 1e-3) / 1e9, 1)
+    pflush = flushed_timing(prefill_attn_only, stream, 50)
+    pflush["TFLOPs"] = round(prefill_flops(w3) / (pflush["median_ms"] * 1e-3) / 1e12, 1)
+    pflush["frac_bf16_peak"] = round(pflush["TFLOPs"] / BF16_DENSE_PEAK_TFLOPS, 4)
+
     dbytes = decode_bytes(w4)
     sbytes = store_bytes(w4)
     flops3 = prefill_flops(w3)
@@ -681,6 +716,8 @@ def main() -> int:
         "prefill_attn_ms": round(pattn_ms, 4),
         "prefill_attn_tflops": round(pattn_tflops, 2),
         "prefill_attn_frac_of_bf16_peak": round(pattn_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+        "decode_attn_flushed": dflush,
+        "prefill_attn_flushed": pflush,
         "rope_store_kv": rope,
         "vocab_embed": vocab,
         "shared_prefix_decode": cascade,
