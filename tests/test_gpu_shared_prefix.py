@@ -98,3 +98,12 @@ def test_decode_split_sizes(oracle_mod, mods, chunk):
     sp = wl.shared_prefix_decode(device="cuda", group_sizes=(20, 12), prefixes=(2500, 640), singles=3,
                                  num_slots=1 << 17)
     _check(oracle_mod, mods, sp, rowsum_reqs=range(0, 35, 4), chunk=chunk)
+
+
+@pytest.mark.parametrize("H,G", [(8, 8), (64, 8)])
+def test_group_sizes_one_and_eight(oracle_mod, mods, H, G):
+    """GQA group sizes 1 and 8: 128 and 16 queries per prefix block."""
+    _, _, wl = mods
+    sp = wl.shared_prefix_decode(device="cuda", group_sizes=(40, 9), prefixes=(1500, 700), singles=2,
+                                 heads=dict(H=H, G=G, d=128), num_slots=1 << 17, q_std=1.0)
+    _check(oracle_mod, mods, sp, rowsum_reqs=range(0, 51, 6))
