@@ -312,6 +312,51 @@ def shared_prefix_leg(iters: int, stream) -> dict:
             "plain_bytes": plain_bytes}
 
 
+def prefill_cpu_baseline(oracle, w, threads: int) -> dict:
+    """The fp64 oracle on a bounded sample of the ragged prefill batch: every
+    4th query row, each as a one-query request at its own position (same
+    page-table row and keys), on all host threads, passes repeated to ~4 s;
+    then every 32nd row on one thread (~2 s).  TFLOP/s of the same
+    algorithmic flops (4 d H per visible key)."""
+    import numpy as np
+    import torch
+
+    kp, vp = oracle.store_kv(w.k_pool.cpu(), w.v_pool.cpu(), w.k_new, w.v_new, w.out_loc)
+    cu = w.cu_q.cpu().numpy()
+    C = w.cached_lens.cpu().numpy()
+    tix_all = w.table_idx.cpu().numpy()
+    q_all = w.q.cpu()
+    pt = w.page_table.cpu()
+
+    def run(step: int, n_threads: int, min_seconds: float):
+        rows = np.arange(0, w.num_tokens, step)
+        b = np.searchsorted(cu, rows, side="right") - 1
+        pos = C[b] + (rows - cu[b])
+        tix = torch.from_numpy(tix_all[b].astype(np.int32))
+        seq = torch.from_numpy((pos + 1).astype(np.int32))
+        qs = torch.arange(len(rows) + 1, dtype=torch.int32)
+        q = q_all[torch.from_numpy(rows)]
+        oracle.set_threads(n_threads)
+        reps, t0 = 0, time.perf_counter()
+        while True:  # repeat the pass until min_seconds of CPU time
+            oracle.attention(q, kp, vp, pt, tix, seq, qs)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                break
+        flops = 4.0 * w.head_dim * w.q_heads * float((pos + 1).sum())
+        return len(rows), el / reps, flops * reps / el / 1e12
+
+    n_all, s_all, tf_all = run(4, threads, 4.0)
+    n_one, s_one, tf_one = run(32, 1, 2.0)
+    oracle.set_threads(threads)
+    return {"value": round(tf_all, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 C oracle, ragged prefill attention of every 4th query row ({n_all} of "
+                      f"{w.num_tokens}), {s_all:.2f} s per pass on {threads} OpenMP threads",
+            "one_thread": {"value": round(tf_one, 6), "unit": "TFLOP/s",
+                           "sample": f"every 32nd query row ({n_one}), {s_one:.2f} s per pass on 1 thread"}}
+
+
 def flushed_timing(fn, stream, iters: int, flush_bytes: int = 1 << 30, warm: int = 3) -> dict:
     """Per-launch times of ``fn`` with a write of ``flush_bytes`` to a scratch
     buffer before each launch (outside the events), so the last-level cache
@@ -683,6 +728,8 @@ def main() -> int:
                          f"{threads} OpenMP threads ({platform.processor() or platform.machine()})",
                "seconds_per_pass": round(cpu_s, 3)}
         log(f"  oracle {cpu_s:.2f}s with {threads} threads")
+        cpu_prefill = prefill_cpu_baseline(oracle, w3, threads)
+        cpu["prefill"] = cpu_prefill
 
     rec = {
         "metric": "paged decode-attn achieved HBM GB/s + req-tokens/s; prefill attn TFLOP/s",
