@@ -217,9 +217,11 @@ MSGL_DEV void attend_range(const int32_t *__restrict__ pt, int tb, int te, int s
     }
 }
 
-// Attend tokens [tb, te) with a software pipeline: page-table ids two
-// iterations ahead and K/V data one iteration ahead of the compute, so every
-// wave keeps loads in flight while it works on the previous tokens.
+// Attend tokens [tb, te) with a software pipeline: page-table ids three
+// iterations ahead and K/V data two iterations ahead of the compute, so every
+// wave keeps two iterations of loads in flight while it works on the previous
+// tokens.  (One iteration ahead fits three 4-wave blocks per CU instead of
+// two, but measured 1.5% slower at batch 256 and 4-6% at batch 32-64.)
 template <typename T, int D, int GQ, int U>
 MSGL_DEV void attend_pipelined(const int32_t *__restrict__ pt, int tb, int te,
                                const T *__restrict__ kbase, const T *__restrict__ vbase,
@@ -231,18 +233,24 @@ MSGL_DEV void attend_pipelined(const int32_t *__restrict__ pt, int tb, int te,
     int s0[U], s1[U], s2[U];
     load_slots<U, RPW>(s0, pt, tb, te, rg);
     load_slots<U, RPW>(s1, pt, tb + TPI, te, rg);
-    uint4 k0[U], v0[U], k1[U], v1[U];
+    int s3[U];
+    load_slots<U, RPW>(s2, pt, tb + 2 * TPI, te, rg);
+    uint4 k0[U], v0[U], k1[U], v1[U], k2[U], v2[U];
     issue_kv<T, U>(k0, v0, s0, kbase, vbase, row_elems, num_slots);
+    issue_kv<T, U>(k1, v1, s1, kbase, vbase, row_elems, num_slots);
     for (int base = tb; base < te; base += TPI) {
-        load_slots<U, RPW>(s2, pt, base + 2 * TPI, te, rg);
-        issue_kv<T, U>(k1, v1, s1, kbase, vbase, row_elems, num_slots);
+        load_slots<U, RPW>(s3, pt, base + 3 * TPI, te, rg);
+        issue_kv<T, U>(k2, v2, s2, kbase, vbase, row_elems, num_slots);
         consume_iter<T, D, GQ, U>(k0, v0, s0, q, scale_log2, st);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             k0[u] = k1[u];
             v0[u] = v1[u];
+            k1[u] = k2[u];
+            v1[u] = v2[u];
             s0[u] = s1[u];
             s1[u] = s2[u];
+            s2[u] = s3[u];
         }
     }
 }
