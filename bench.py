@@ -510,11 +510,43 @@ def prefill_profile(iters: int) -> int:
     return 0
 
 
+def ceilings(iters: int) -> int:
+    """Measured ceilings beside the vendor peaks: a large bf16 GEMM through the
+    vendor BLAS (torch.matmul, 2-D contiguous operands) and a plain device copy
+    (read once, write once).  One JSON line each."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    for n in (8192, 16384):
+        a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+        b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+        c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        with torch.cuda.stream(stream):
+            ms = _time_stream(lambda: torch.matmul(a, b, out=c), stream, iters, warm=20)
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"ceiling": "bf16 gemm (torch.matmul)", "m=n=k": n, "ms": round(ms, 4),
+                          "TFLOPs": round(tf, 1), "frac_bf16_peak": round(tf / BF16_DENSE_PEAK_TFLOPS, 4)}),
+              flush=True)
+        del a, b, c
+    n = (2 << 30) // 4
+    x = torch.ones(n, device=dev)
+    y = torch.empty_like(x)
+    with torch.cuda.stream(stream):
+        ms = _time_stream(lambda: y.copy_(x), stream, iters, warm=5)
+    gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+    print(json.dumps({"ceiling": "device copy (torch copy_, 2 GiB read + 2 GiB written)", "ms": round(ms, 4),
+                      "GBs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+    return 0
+
+
 def main() -> int:
     if len(sys.argv) > 1 and sys.argv[1] == "--prefill-profile":
         return prefill_profile(int(sys.argv[2]) if len(sys.argv) > 2 else 20)
     if len(sys.argv) > 1 and sys.argv[1] == "--mixed":
         return mixed(int(sys.argv[2]) if len(sys.argv) > 2 else 5)
+    if len(sys.argv) > 1 and sys.argv[1] == "--ceilings":
+        return ceilings(int(sys.argv[2]) if len(sys.argv) > 2 else 20)
     if len(sys.argv) > 1 and sys.argv[1] == "--sweep":
         return sweep(int(sys.argv[2]) if len(sys.argv) > 2 else 20)
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
