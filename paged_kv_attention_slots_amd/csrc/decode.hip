@@ -6,9 +6,13 @@
 // partials, page-table ids) is small beside them.
 //
 // Work decomposition (balanced split).  Concatenate every request's keys into
-// one sequence of sum(seq_lens) tokens (per group of kv heads when there are
-// more kv heads than waves in a block) and give each block of the persistent
-// grid an equal, contiguous share of it.  A block has one wave per kv head;
+// one sequence (per group of kv heads when there are more kv heads than waves
+// in a block), each request preceded by kPieceUnits units of fixed cost, and
+// give each block of the persistent grid an equal, contiguous share of it.
+// The fixed cost stands for what a piece costs beyond its keys (its q, page
+// table and K/V round trips, the reductions, the write), so a run of
+// one-key requests (padded rows of a captured batch) spreads over blocks
+// instead of queueing in one.  A block has one wave per kv head;
 // each wave streams its share of tokens for its head with a software pipeline
 // (attend_valu.h) and no barriers.  Where a block's share covers a request
 // whole, the wave writes the normalised output; where a request straddles
@@ -25,9 +29,12 @@
 
 namespace msgl {
 
+// Work units a request costs beyond its keys (see above).
+constexpr int kPieceUnits = 32;
+
 // Workspace layout (offsets in bytes):
-//   [0, 256)            control: int64 total tokens, int64 share per block
-//   [256, 256 + P)      int32 prefix of lengths [batch + 1], P rounded up to 256
+//   [0, 256)            control: int64 total work units, int64 share per block
+//   [256, 256 + P)      int32 prefix of work units [batch + 1], P rounded up to 256
 //   then                float part_o [batch + kMaxDecodeGrid][q_heads][head_dim]
 //   then                float part_ml[batch + kMaxDecodeGrid][q_heads][2]
 // A piece (request b, block j) is stored at index b + j: pieces are
@@ -38,7 +45,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
     using Geo = Geometry<T, D>;
     constexpr int E = Geo::kEpl;
     constexpr int LPR = Geo::kLpr;
-    extern __shared__ int s_tok[];  // [batch + 1] tokens before each request
+    extern __shared__ int s_tok[];  // [batch + 1] work units before each request
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -57,6 +64,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
         for (int base = 0; base < a.batch; base += 64) {
             const int b = base + lane;
             int n = b < a.batch ? max(0, min(a.seq_lens[b], lmax) - (a.key_start ? max(0, a.key_start[b]) : 0)) : 0;
+            n = n > 0 ? n + kPieceUnits : 0;  // a request's work: its keys plus a fixed cost
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const int y = __shfl_up(n, off);
@@ -90,11 +98,15 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
         if (s_tok[mid] <= off) lo = mid; else hi = mid;
     }
     int b = lo;
-    int j = (int)(off - s_tok[b]);
+    int u = (int)(off - s_tok[b]);  // work unit within request b
 
     while (cur < end) {
-        const int L = s_tok[b + 1] - s_tok[b];
-        const int je = (int)min((int64_t)L, (int64_t)j + (end - cur));
+        // request b's units: kPieceUnits of fixed cost, then one per key
+        const int W = s_tok[b + 1] - s_tok[b];
+        const int L = W > 0 ? W - kPieceUnits : 0;
+        const int ue = (int)min((int64_t)W, (int64_t)u + (end - cur));
+        const int j = max(u - kPieceUnits, 0);
+        const int je = max(ue - kPieceUnits, 0);
         if (je > j) {
             const int kvh = hg * wpb + wave;
             const int32_t *pt = a.page_table + (int64_t)a.table_idx[b] * a.row_stride +
@@ -149,10 +161,10 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
                 }
             }
         }
-        cur += je - j;
-        j = je;
-        if (j >= L) {
-            j = 0;
+        cur += ue - u;
+        u = ue;
+        if (u >= W) {
+            u = 0;
             if (++b == a.batch) {
                 b = 0;
                 ++hg;
@@ -191,10 +203,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     if (h >= a.q_heads) return;
     const int64_t total = a.ctrl[0];
     const int64_t share = a.ctrl[1];
-    const int L = a.prefix[b + 1] - a.prefix[b];
+    const int W = a.prefix[b + 1] - a.prefix[b];
+    const int L = W - kPieceUnits;  // its keys
     if (L <= 0) return;
     const int hg = (h / GQ) / a.wpb;
-    const int64_t first_tok = (int64_t)hg * total + a.prefix[b];
+    const int64_t first_tok = (int64_t)hg * total + a.prefix[b] + kPieceUnits;  // its first key's unit
     const int first = (int)(first_tok / share);
     const int last = (int)((first_tok + L - 1) / share);
     if (first == last) return;  // one piece: the split kernel wrote the output
