@@ -66,3 +66,37 @@ def test_prefill_single_new_tokens_and_full_row(oracle_mod, mods):
                           seq_lens=lens, cached_lens=cached, seed=78, q_std=1.0, device="cuda")
     assert max(lens) == w.row_stride
     _check(oracle_mod, runner, w)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 1024])
+def test_decode_many_one_key_requests(oracle_mod, mods, chunk):
+    """The decode split counts each request as its keys plus a fixed cost of
+    work units; blocks whose share covers only a request's fixed-cost units
+    must skip it, and the merge must find exactly the blocks holding its keys.
+    A batch of one-key requests interleaved with long ones and lengths around
+    the fixed cost (31, 32, 33, 64, 65) covers those boundaries."""
+    runner, wl = mods
+    rng = np.random.default_rng(79)
+    lens = []
+    for i in range(160):
+        lens.append(1 if i % 3 else int(rng.choice([2, 31, 32, 33, 64, 65, 700, 5000, 20000])))
+    S = 1 << 19
+    rows = wl.rows_from_free_slots(rng.permutation(S), lens)
+    w = wl.build_workload("decode-one-key-mix", "decode", torch.bfloat16, **wl.QWEN3_8B, page_size=1,
+                          num_slots=S, max_running_req=len(lens), max_seq_len=20000, rows=rows, seq_lens=lens,
+                          cached_lens=[L - 1 for L in lens], seed=79, q_std=1.0, device="cuda")
+    say(f"[edges] one-key mix: {len(lens)} requests, {sum(lens)} keys, chunk {chunk}")
+    res = runner.run_step(w, chunk=chunk)
+    torch.cuda.synchronize()
+    kp, vp, out_ref, lse_ref = oracle_mod.step(w)
+    assert store_mismatch(w, res.k_pool, res.v_pool, kp, vp) == 0
+    err = max_abs(res.out, out_ref)
+    lse_err = max_abs(res.lse, lse_ref)
+    say(f"[edges] one-key mix chunk {chunk}: max-abs {err:.3e} lse {lse_err:.2e}")
+    assert err <= BF16_TOL and lse_err < 1e-3, (err, lse_err)
+    # a one-key request returns its V row exactly (up to the bf16 rounding of V itself)
+    one = [b for b, L in enumerate(lens) if L == 1][:20]
+    for b in one:
+        slot = int(w.page_table[int(w.table_idx[b]), 0])
+        v = vp[slot].repeat_interleave(w.q_heads // w.kv_heads, dim=0)
+        assert torch.equal(res.out[b].cpu().view(torch.int16), v.view(torch.int16)), b
