@@ -227,8 +227,8 @@ msgl_status msgl_prefill_attn(void *out, float *lse, const void *q, const void *
                               msgl_dtype dtype, void *stream);
 
 /*
- * Decode step as a captured HIP graph (store_kv, then decode attention), for
- * one padded batch size, after the CUDA-Graph runner of the Stage 4 milestone:
+ * Decode step as a captured HIP graph (the KV write, then decode attention),
+ * for one padded batch size, after the CUDA-Graph runner of the Stage 4 milestone:
  * every input lives in a fixed buffer whose address is recorded at capture;
  * before each replay the caller writes the step's values into those buffers
  * (rows beyond the real batch use the dummy request: seq_len 1, table row =
@@ -236,7 +236,10 @@ msgl_status msgl_prefill_attn(void *out, float *lse, const void *q, const void *
  * stay allocated, at the same addresses, for the graph's lifetime.
  * `stream` must not be the null stream (capture needs a real stream).
  * Arguments mean what they mean in msgl_store_kv and msgl_decode_attn with
- * num_tokens == batch == padded_batch.
+ * num_tokens == batch == padded_batch.  In the graph the KV write rides in the
+ * decode kernel: the wave that reads a request's last key (its new token,
+ * out_loc[b] == page_table[table_idx[b], seq_lens[b] - 1]) writes that row
+ * first, so a replay runs two kernels instead of three.
  */
 typedef struct msgl_graph msgl_graph;
 

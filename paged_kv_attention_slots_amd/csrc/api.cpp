@@ -114,6 +114,12 @@ msgl::DecodeArgs decode_args(void *out, float *lse, const void *q, const void *k
     a.part_ml = a.part_o + pieces * q_heads * head_dim;
     a.key_start = nullptr;
     a.out_f32 = 0;
+    a.fuse_store = 0;
+    a.k_pool_w = nullptr;
+    a.v_pool_w = nullptr;
+    a.k_new = nullptr;
+    a.v_new = nullptr;
+    a.out_loc = nullptr;
     return a;
 }
 
@@ -377,18 +383,23 @@ msgl_status msgl_decode_graph_create(msgl_graph **graph, void *k_pool, void *v_p
                      workspace, workspace_bytes);
     if (s != MSGL_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    msgl::StoreKvArgs sa = store_args(k_pool, v_pool, num_slots, kv_heads, head_dim, dtype, k_new, v_new, out_loc,
-                                      padded_batch);
     msgl::DecodeArgs da = decode_args(out, lse, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx,
                                       seq_lens, padded_batch, q_heads, kv_heads, head_dim, max_seq_len,
                                       chunk, sm_scale, workspace);
+    // the KV write rides in the split kernel: the wave that reads a request's
+    // last key writes that key's row first (one kernel fewer per replay)
+    da.fuse_store = 1;
+    da.k_pool_w = k_pool;
+    da.v_pool_w = v_pool;
+    da.k_new = k_new;
+    da.v_new = v_new;
+    da.out_loc = out_loc;
     hipError_t e = msgl::launch_decode(da, static_cast<msgl::DType>(dtype), head_dim, st, true);
     if (e != hipSuccess) return from_hip(e, "decode preparation");
     e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return from_hip(e, "hipStreamBeginCapture");
-    hipError_t e1 = msgl::launch_store_kv(sa, st);
-    hipError_t e2 = e1 == hipSuccess ? msgl::launch_decode(da, static_cast<msgl::DType>(dtype), head_dim, st)
-                                     : hipSuccess;
+    hipError_t e1 = hipSuccess;
+    hipError_t e2 = msgl::launch_decode(da, static_cast<msgl::DType>(dtype), head_dim, st);
     hipGraph_t g = nullptr;
     e = hipStreamEndCapture(st, &g);
     if (e1 != hipSuccess || e2 != hipSuccess || e != hipSuccess) {

@@ -120,6 +120,20 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeArgs a) {
             st.init();
             const T *kb = reinterpret_cast<const T *>(a.k_pool) + (int64_t)kvh * D + lr * E;
             const T *vb = reinterpret_cast<const T *>(a.v_pool) + (int64_t)kvh * D + lr * E;
+            if (a.fuse_store && je == L && rg == 0) {
+                // the KV write of this request's new token (its last key), this
+                // wave's head: only the piece holding that key reads it, and it
+                // reads it after this store, from the same wave
+                const int64_t slot = a.out_loc[b];
+                if (slot >= 0 && slot < a.num_slots) {
+                    const int64_t src = ((int64_t)b * a.kv_heads + kvh) * D + lr * E;
+                    const int64_t dst = slot * row_elems + (int64_t)kvh * D + lr * E;
+                    st16(static_cast<T *>(a.k_pool_w) + dst, ld16(static_cast<const T *>(a.k_new) + src));
+                    st16(static_cast<T *>(a.v_pool_w) + dst, ld16(static_cast<const T *>(a.v_new) + src));
+                }
+            }
+            if (a.fuse_store && je == L)  // the row is written before any lane of the wave reads it
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             attend_pipelined<T, D, GQ, U>(pt, j, je, kb, vb, row_elems, (uint32_t)a.num_slots, q,
                                           a.scale_log2, rg, st);
             st.template reduce_wave<LPR>();

@@ -86,6 +86,15 @@ struct DecodeArgs {
     float *part_ml;       // [batch + kMaxDecodeGrid, q_heads, 2]  (max in log2 units, sum)
     const int32_t *key_start;  // nullable: request b attends keys key_start[b] .. seq_lens[b]-1
     int32_t out_f32;      // nonzero: out is float32 whatever the storage type
+    // nonzero: the split kernel also writes request b's new K/V row (k_new[b],
+    // v_new[b]) to slot out_loc[b] of k_pool_w / v_pool_w (the same pools as
+    // k_pool / v_pool) before it reads that request's last key
+    int32_t fuse_store;
+    void *k_pool_w;
+    void *v_pool_w;
+    const void *k_new;
+    const void *v_new;
+    const int32_t *out_loc;
 };
 
 struct PrefillArgs {
