@@ -782,7 +782,7 @@ def main() -> int:
             "decode": {"batch": w4.bs, "q_heads": w4.q_heads, "kv_heads": w4.kv_heads,
                        "head_dim": w4.head_dim, "page_size": w4.page_size,
                        "context_tokens": int(w4.seq_lens.sum()), "max_len": int(w4.seq_lens.max()),
-                       "min_keys_per_block": args.chunk or 128},
+                       "min_units_per_block": args.chunk or 64},
             "prefill": {"requests": w3.bs, "q_heads": w3.q_heads, "kv_heads": w3.kv_heads,
                         "head_dim": w3.head_dim, "extend_tokens": w3.num_tokens,
                         "context_tokens": int(w3.seq_lens.sum())},

@@ -144,7 +144,7 @@ msgl_status msgl_vocab_embed(void *out, const void *weight, int64_t vocab_start,
  * its keys plus a fixed cost of 32 key-equivalents, so runs of very short
  * requests spread out), are cut into equal contiguous shares, one per block of
  * a grid sized to the device; `chunk` (a multiple of 64; 0 picks the library
- * default, 128) is the least number of such units a share holds, so small
+ * default, 64) is the least number of such units a share holds, so small
  * batches do not split below it.  The
  * pieces' partial softmax states are merged afterwards; the result does not
  * depend on the split beyond float32 rounding.  max_seq_len bounds every seq_lens[b]

@@ -12,7 +12,7 @@ enum DType { kF32 = 0, kBF16 = 1 };
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 // Minimum keys per decode block (the `chunk` argument) when the caller passes 0.
-constexpr int kDefaultChunk = 128;
+constexpr int kDefaultChunk = 64;
 // Bytes of the decode workspace's control block.
 constexpr size_t kCtrlBytes = 256;
 // Upper bound of the decode grid (it sizes the workspace's partial states).
