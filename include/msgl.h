@@ -268,8 +268,10 @@ void msgl_graph_destroy(msgl_graph *graph);
  * every page-table entry a request uses lies in [0, num_slots); when
  * page_size > 1, the entries of each page are consecutive and the page's
  * first entry is a multiple of page_size; when out_loc is given (num_tokens
- * entries), out_loc entries lie in [0, num_slots) and no slot other than
- * `dummy_slot` repeats (pass -1 to allow no repeats).
+ * entries), it lists page_table[table_idx[b], cached_lens[b] .. seq_lens[b]-1]
+ * for b in order (one entry per new token; the captured decode step relies on
+ * it), its entries lie in [0, num_slots) and no slot other than `dummy_slot`
+ * repeats (pass -1 to allow no repeats).
  * cached_lens and cu_q may be NULL (decode: cached = seq_len - 1).
  * Returns MSGL_OK or MSGL_INVALID_ARG with the first violation in
  * msgl_last_error.

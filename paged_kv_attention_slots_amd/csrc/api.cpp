@@ -508,6 +508,21 @@ msgl_status msgl_validate_batch(const int32_t *page_table, int32_t rows, int32_t
         }
     }
     if (out_loc) {
+        // out_loc is page_table[row, cached:len] of each request, in batch order
+        // (decode, cached_lens NULL: one token per request, its last key)
+        int64_t t = 0;
+        for (int32_t b = 0; b < batch && t < num_tokens; ++b) {
+            const int32_t L = seq_lens[b];
+            const int32_t C = cached_lens ? cached_lens[b] : L - 1;
+            const int32_t *row = page_table + (int64_t)table_idx[b] * row_stride;
+            for (int32_t i = C; i < L && t < num_tokens; ++i, ++t)
+                if (out_loc[t] != row[i])
+                    return fail(MSGL_INVALID_ARG, "out_loc[%lld] = %d, expected page_table[%d, %d] = %d", (long long)t,
+                                out_loc[t], table_idx[b], i, row[i]);
+        }
+        if (t != num_tokens)
+            return fail(MSGL_INVALID_ARG, "out_loc has %d entries, the batch's new tokens are %lld", num_tokens,
+                        (long long)t);
         std::vector<unsigned char> seen((size_t)num_slots, 0);
         for (int32_t t = 0; t < num_tokens; ++t) {
             const int32_t s = out_loc[t];

@@ -218,3 +218,27 @@ def test_shared_prefix_validator_rejects():
     pl = sp.prefix_lens.clone()
     pl[5] = 3  # the single request is in no group
     assert "in no group" in bad(pl=pl)
+
+
+def test_validator_checks_out_loc_against_page_table():
+    """out_loc must be page_table[row, cached:len] of each request in order:
+    the captured decode step writes the new token's row where the request's
+    last key is read."""
+    from paged_kv_attention_slots_amd import _lib as L
+
+    w = wl.qwen3_06b_decode(bs=6, lo=20, hi=60, num_slots=4096)
+    args = dict(max_seq_len=w.max_seq_len, num_slots=w.num_slots, page_size=1, dummy_slot=w.dummy_slot)
+    L.msgl_validate_batch(w.page_table, w.table_idx, w.seq_lens, None, None, out_loc=w.out_loc, **args)
+    loc = w.out_loc.clone()
+    loc[[1, 2]] = loc[[2, 1]]  # two requests' new slots swapped
+    with pytest.raises(L.MsglError, match="expected page_table"):
+        L.msgl_validate_batch(w.page_table, w.table_idx, w.seq_lens, None, None, out_loc=loc, **args)
+    with pytest.raises(L.MsglError, match="entries"):
+        L.msgl_validate_batch(w.page_table, w.table_idx, w.seq_lens, None, None, out_loc=w.out_loc[:4], **args)
+    p = wl.ragged_prefill(n_req=3, e_lo=5, e_hi=20, c_hi=10, num_slots=1024)
+    pargs = dict(max_seq_len=p.max_seq_len, num_slots=p.num_slots, page_size=1)
+    L.msgl_validate_batch(p.page_table, p.table_idx, p.seq_lens, p.cached_lens, p.cu_q, out_loc=p.out_loc, **pargs)
+    loc = p.out_loc.clone()
+    loc[0] = loc[0] + 1 if int(loc[0]) + 1 < p.num_slots else loc[0] - 1
+    with pytest.raises(L.MsglError, match="expected page_table"):
+        L.msgl_validate_batch(p.page_table, p.table_idx, p.seq_lens, p.cached_lens, p.cu_q, out_loc=loc, **pargs)
