@@ -510,6 +510,11 @@ msgl_status msgl_validate_batch(const int32_t *page_table, int32_t rows, int32_t
     if (out_loc) {
         // out_loc is page_table[row, cached:len] of each request, in batch order
         // (decode, cached_lens NULL: one token per request, its last key)
+        int64_t expected = 0;
+        for (int32_t b = 0; b < batch; ++b) expected += seq_lens[b] - (cached_lens ? cached_lens[b] : seq_lens[b] - 1);
+        if (expected != num_tokens)
+            return fail(MSGL_INVALID_ARG, "out_loc has %d entries, the batch's new tokens are %lld", num_tokens,
+                        (long long)expected);
         int64_t t = 0;
         for (int32_t b = 0; b < batch && t < num_tokens; ++b) {
             const int32_t L = seq_lens[b];
@@ -520,9 +525,6 @@ msgl_status msgl_validate_batch(const int32_t *page_table, int32_t rows, int32_t
                     return fail(MSGL_INVALID_ARG, "out_loc[%lld] = %d, expected page_table[%d, %d] = %d", (long long)t,
                                 out_loc[t], table_idx[b], i, row[i]);
         }
-        if (t != num_tokens)
-            return fail(MSGL_INVALID_ARG, "out_loc has %d entries, the batch's new tokens are %lld", num_tokens,
-                        (long long)t);
         std::vector<unsigned char> seen((size_t)num_slots, 0);
         for (int32_t t = 0; t < num_tokens; ++t) {
             const int32_t s = out_loc[t];
