@@ -312,6 +312,17 @@ def shared_prefix_leg(iters: int, stream) -> dict:
             "plain_bytes": plain_bytes}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def prefill_cpu_baseline(oracle, w, threads: int) -> dict:
     """The fp64 oracle on a bounded sample of the ragged prefill batch: every
     4th query row, each as a one-query request at its own position (same
@@ -757,7 +768,8 @@ def main() -> int:
         cpu = {"value": round(sb / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"fp64 C oracle, decode attention of the first {n} of {w4.bs} requests "
                          f"({int(ws.seq_lens.sum())} context tokens), {reps} passes, {cpu_s:.2f} s each on "
-                         f"{threads} OpenMP threads ({platform.processor() or platform.machine()})",
+                         f"{threads} OpenMP threads ({cpu_model()}; {len(os.sched_getaffinity(0))} cores "
+                         f"in this process's affinity set)",
                "seconds_per_pass": round(cpu_s, 3)}
         log(f"  oracle {cpu_s:.2f}s with {threads} threads")
         cpu_prefill = prefill_cpu_baseline(oracle, w3, threads)
