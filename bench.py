@@ -25,6 +25,7 @@ import json
 import math
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -691,6 +692,43 @@ def main() -> int:
     torch.cuda.synchronize()
     pattn_ms = ka.elapsed_time(kb) / args.kernel_iters
 
+    # the same launch with the host plan (block list made on the host, copied
+    # once): bit-identical outputs, timed in interleaved rounds with the
+    # unplanned launch
+    log("timing the planned prefill launch (host plan)")
+    h0 = time.perf_counter()
+    plan_h = _lib.msgl_prefill_plan(w3.seq_lens.cpu(), w3.cached_lens.cpu(), w3.cu_q.cpu(), w3.table_idx.cpu(),
+                                    w3.page_table.shape[0], w3.page_table.shape[1], w3.q_heads, w3.kv_heads)
+    plan_us = (time.perf_counter() - h0) * 1e6
+    plan_d = plan_h.to(dev)
+    out3p = torch.empty_like(out3)
+    lse3p = torch.empty_like(lse3)
+
+    def prefill_attn_planned():
+        _lib.msgl_prefill_attn_planned(out3p, lse3p, w3.q, w3.k_pool, w3.v_pool, w3.page_table, plan_h, plan_d,
+                                       page_size=w3.page_size, sm_scale=w3.sm_scale, stream=stream)
+
+    prefill_attn_planned()
+    torch.cuda.synchronize()
+    plan_same = bool(torch.equal(out3p.view(torch.int16), out3.view(torch.int16)) and torch.equal(lse3p, lse3))
+    rounds = {"planned": [], "unplanned": []}
+    n_round = max(100, args.kernel_iters)
+    for _ in range(4):
+        for tag, fn in (("planned", prefill_attn_planned), ("unplanned", prefill_attn_only)):
+            for _ in range(n_round):  # the clocks stay up: no idle gap before the timed launches
+                fn()
+            ka.record(stream)
+            for _ in range(n_round):
+                fn()
+            kb.record(stream)
+            torch.cuda.synchronize()
+            rounds[tag].append(ka.elapsed_time(kb) / n_round)
+    plan_ms = statistics.median(rounds["planned"])
+    planned = {"median_ms": round(plan_ms, 4), "tflops": round(prefill_flops(w3) / (plan_ms * 1e-3) / 1e12, 1),
+               "unplanned_median_ms": round(statistics.median(rounds["unplanned"]), 4),
+               "rounds": 4, "launches_per_round": n_round, "entries": int(plan_h[3]),
+               "host_plan_us": round(plan_us, 1), "bit_identical": plan_same}
+
     # the next step on the layer's path: RoPE of q and k fused with the KV write,
     # on the decode batch and on the prefill batch (back-to-back launches)
     log(f"timing {args.kernel_iters} fused RoPE + KV-write launches per batch")
@@ -807,6 +845,7 @@ def main() -> int:
         "prefill_attn_ms": round(pattn_ms, 4),
         "prefill_attn_tflops": round(pattn_tflops, 2),
         "prefill_attn_frac_of_bf16_peak": round(pattn_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+        "prefill_attn_planned": planned,
         "decode_attn_flushed": dflush,
         "prefill_attn_flushed": pflush,
         "rope_store_kv": rope,

@@ -227,6 +227,56 @@ msgl_status msgl_prefill_attn(void *out, float *lse, const void *q, const void *
                               msgl_dtype dtype, void *stream);
 
 /*
+ * Host plan / run split of the prefill call, after the plan-then-run structure
+ * of the FlashInfer backend that the Stage 4 milestone's engine uses: the
+ * block list that msgl_prefill_attn derives on the device from the lengths
+ * (every (request, query block) pair, the most key tiles first, ties in
+ * request order, one launch block per entry and kv head) is made on the host
+ * instead, from host copies of the batch metadata, before the step.  The run
+ * reads its work item from that list, so no block enumerates the batch, and
+ * the batch may exceed the 1024 requests the device enumeration serves on the
+ * matrix-core path.  The results equal msgl_prefill_attn's bit for bit.
+ * bf16 and head_dim 128 only (else MSGL_UNSUPPORTED).
+ *
+ * msgl_prefill_plan_bytes: the plan buffer size that suffices for any batch of
+ * these sizes (0 for invalid sizes).
+ *
+ * msgl_prefill_plan: every pointer is HOST memory.  seq_lens, cached_lens,
+ * table_idx [batch] and cu_q [batch + 1] mean what they mean in
+ * msgl_prefill_attn; rows is the page table's row count.  Checks the batch
+ * (cu_q[0] == 0, cu_q[batch] == total_q, cu_q[b+1] - cu_q[b] >= 1 ==
+ * seq_lens[b] - cached_lens[b], cached_lens[b] >= 0, seq_lens[b] <= row_stride,
+ * 0 <= table_idx[b] < rows) and writes the plan: a header of 8 int32 (a magic
+ * number, the layout, query tokens per block, the entry count, batch, total_q,
+ * q_heads, kv_heads), then 8 int32 per entry (request, query block, new tokens,
+ * cached tokens, first q row, table row, key tiles, 0).  MSGL_INVALID_ARG on a
+ * malformed batch, MSGL_WORKSPACE_TOO_SMALL when plan_bytes is short; nothing
+ * is written on error except possibly the buffer's contents.
+ *
+ * msgl_prefill_attn_planned: plan_host is the plan as written (read on the
+ * host for the launch size and layout); plan_dev a device copy of the same
+ * bytes that the kernels read, which must stay unchanged until the launch has
+ * run.  The plan's heads must equal q_heads and kv_heads.  The other arguments
+ * are those of msgl_prefill_attn; the device arrays of the batch (seq_lens,
+ * cached_lens, cu_q, table_idx) are not needed: the plan carries them.
+ */
+size_t msgl_prefill_plan_bytes(int32_t batch, int32_t total_q, int32_t q_heads, int32_t kv_heads);
+
+msgl_status msgl_prefill_plan(int32_t *plan, size_t plan_bytes, const int32_t *seq_lens,
+                              const int32_t *cached_lens, const int32_t *cu_q,
+                              const int32_t *table_idx, int32_t batch, int32_t total_q,
+                              int32_t rows, int32_t row_stride, int32_t q_heads, int32_t kv_heads,
+                              int32_t head_dim, msgl_dtype dtype);
+
+msgl_status msgl_prefill_attn_planned(void *out, float *lse, const void *q, const void *k_pool,
+                                      const void *v_pool, int64_t num_slots,
+                                      const int32_t *page_table, int32_t row_stride,
+                                      int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                      int32_t page_size, float sm_scale, msgl_dtype dtype,
+                                      const int32_t *plan_host, const int32_t *plan_dev,
+                                      size_t plan_bytes, void *stream);
+
+/*
  * Decode step as a captured HIP graph (the KV write, then decode attention),
  * for one padded batch size, after the CUDA-Graph runner of the Stage 4 milestone:
  * every input lives in a fixed buffer whose address is recorded at capture;

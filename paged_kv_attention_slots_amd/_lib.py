@@ -33,7 +33,8 @@ EXPORTS = (
     "msgl_decode_workspace_bytes",
     "msgl_decode_attn", "msgl_prefill_attn", "msgl_decode_graph_create", "msgl_graph_launch",
     "msgl_graph_destroy", "msgl_validate_batch", "msgl_decode_shared_prefix_workspace_bytes",
-    "msgl_decode_attn_shared_prefix", "msgl_validate_shared_prefix",
+    "msgl_decode_attn_shared_prefix", "msgl_validate_shared_prefix", "msgl_prefill_plan_bytes",
+    "msgl_prefill_plan", "msgl_prefill_attn_planned",
 )
 
 
@@ -74,6 +75,13 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msgl_prefill_attn.restype = st
     lib.msgl_prefill_attn.argtypes = [P, P, P, P, P, I64, P, I32, P, P, P, P, I32, I32, I32, I32, I32,
                                       I32, I32, F, st, P]
+    lib.msgl_prefill_plan_bytes.restype = SZ
+    lib.msgl_prefill_plan_bytes.argtypes = [I32, I32, I32, I32]
+    lib.msgl_prefill_plan.restype = st
+    lib.msgl_prefill_plan.argtypes = [P, SZ, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, st]
+    lib.msgl_prefill_attn_planned.restype = st
+    lib.msgl_prefill_attn_planned.argtypes = [P, P, P, P, P, I64, P, I32, I32, I32, I32, I32, F, st, P, P, SZ,
+                                              P]
     lib.msgl_decode_graph_create.restype = st
     lib.msgl_decode_graph_create.argtypes = [ctypes.POINTER(P), P, P, I64, P, P, P, P, P, P, P, I32, P,
                                              P, I32, I32, I32, I32, I32, I32, I32, F, st, P, SZ, P]
@@ -230,6 +238,52 @@ def msgl_prefill_attn(out, lse, q, k_pool, v_pool, page_table, table_idx, seq_le
                                  _p(_i32(seq_lens)), _p(_i32(cached_lens)), _p(_i32(cu_q)),
                                  table_idx.numel(), T, max_extend, H, G, d, page_size, sm_scale,
                                  _dt(q), _stream(stream)))
+
+
+def msgl_prefill_plan_bytes(batch: int, total_q: int, q_heads: int, kv_heads: int) -> int:
+    return int(lib.msgl_prefill_plan_bytes(batch, total_q, q_heads, kv_heads))
+
+
+def _host_i32(t) -> torch.Tensor:
+    t = torch.as_tensor(t)
+    if t.dtype != torch.int32:
+        raise TypeError(f"index tensors are int32, got {t.dtype}")
+    return t.cpu().contiguous()
+
+
+def msgl_prefill_plan(seq_lens, cached_lens, cu_q, table_idx, rows: int, row_stride: int, q_heads: int,
+                      kv_heads: int, head_dim: int = 128, dtype: int = MSGL_BF16) -> torch.Tensor:
+    """Host plan of a prefill launch from host copies of the batch metadata.
+
+    Returns the plan as a CPU int32 tensor (header, then one entry per query
+    block, in launch order); copy it to the GPU for msgl_prefill_attn_planned.
+    """
+    sl, cl, cq, ti = (_host_i32(x) for x in (seq_lens, cached_lens, cu_q, table_idx))
+    batch = ti.numel()
+    total_q = int(cq[-1]) if cq.numel() else 0
+    nbytes = msgl_prefill_plan_bytes(batch, total_q, q_heads, kv_heads)
+    if nbytes == 0:
+        raise MsglError(MSGL_INVALID_ARG, "invalid plan sizes")
+    plan = torch.zeros(nbytes // 4, dtype=torch.int32)
+    _check(lib.msgl_prefill_plan(_p(plan, device=False), nbytes, _p(sl, device=False), _p(cl, device=False),
+                                 _p(cq, device=False), _p(ti, device=False), batch, total_q, rows, row_stride,
+                                 q_heads, kv_heads, head_dim, dtype))
+    return plan[: 8 + 8 * int(plan[3])].clone()
+
+
+def msgl_prefill_attn_planned(out, lse, q, k_pool, v_pool, page_table, plan_host: torch.Tensor,
+                              plan_dev: torch.Tensor, page_size: int = 1, sm_scale: Optional[float] = None,
+                              stream=None) -> None:
+    H, d = q.shape[1], q.shape[2]
+    S, G, _ = k_pool.shape
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    if plan_dev.numel() < plan_host.numel():
+        raise ValueError("the device plan is shorter than the host plan")
+    _check(lib.msgl_prefill_attn_planned(_p(out), _p(lse), _p(q), _p(k_pool), _p(v_pool), S,
+                                         _p(_i32(page_table)), page_table.shape[1], H, G, d, page_size,
+                                         sm_scale, _dt(q), _p(_host_i32(plan_host), device=False),
+                                         _p(_i32(plan_dev)), plan_host.numel() * 4, _stream(stream)))
 
 
 class DecodeGraph:

@@ -3,6 +3,7 @@
 // validator.  Nothing here allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -356,9 +357,127 @@ msgl_status msgl_prefill_attn(void *out, float *lse, const void *q, const void *
     a.splits = 1;
     a.part_o = nullptr;
     a.part_lse = nullptr;
+    a.plan = nullptr;
     return from_hip(msgl::launch_prefill(a, static_cast<msgl::DType>(dtype), head_dim,
                                          static_cast<hipStream_t>(stream)),
                     "prefill launch");
+}
+
+// ---------------------------------------------------------------------------
+// Host plan of a prefill launch: the block list that the kernel would otherwise
+// derive on the device from the lengths (every (request, query block) pair,
+// the most key tiles first, ties in request order), made on the host from the
+// host copies of the batch metadata.
+
+size_t msgl_prefill_plan_bytes(int32_t batch, int32_t total_q, int32_t q_heads, int32_t kv_heads) {
+    if (batch < 0 || total_q < 0 || kv_heads < 1 || q_heads < kv_heads || q_heads % kv_heads != 0) return 0;
+    const int64_t bq = msgl::prefill_small_bq(q_heads / kv_heads);
+    const int64_t entries = ((int64_t)total_q + (int64_t)batch * (bq - 1)) / bq;  // >= sum_b ceil(E_b / bq)
+    return (size_t)(msgl::kPlanHeaderInts + entries * msgl::kPlanEntryInts) * sizeof(int32_t);
+}
+
+msgl_status msgl_prefill_plan(int32_t *plan, size_t plan_bytes, const int32_t *seq_lens,
+                              const int32_t *cached_lens, const int32_t *cu_q, const int32_t *table_idx,
+                              int32_t batch, int32_t total_q, int32_t rows, int32_t row_stride,
+                              int32_t q_heads, int32_t kv_heads, int32_t head_dim, msgl_dtype dtype) {
+    if (dtype != MSGL_BF16 || head_dim != 128)
+        return fail(MSGL_UNSUPPORTED, "the planned prefill runs the bf16 matrix-core kernels (head_dim 128)");
+    msgl_status s = check_common(dtype, head_dim, kv_heads, 1);
+    if (s != MSGL_OK) return s;
+    if ((s = check_group(q_heads, kv_heads)) != MSGL_OK) return s;
+    if (batch < 0 || total_q < 0) return fail(MSGL_INVALID_ARG, "negative batch or total_q");
+    if (!plan || (batch > 0 && (!seq_lens || !cached_lens || !cu_q || !table_idx)))
+        return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    if (rows < 1 || row_stride < 1) return fail(MSGL_INVALID_ARG, "rows %d or row_stride %d < 1", rows, row_stride);
+    if (batch == 0 && total_q != 0) return fail(MSGL_INVALID_ARG, "total_q %d without requests", total_q);
+    if (batch > 0 && cu_q[0] != 0) return fail(MSGL_INVALID_ARG, "cu_q[0] = %d, not 0", cu_q[0]);
+    if (batch > 0 && cu_q[batch] != total_q)
+        return fail(MSGL_INVALID_ARG, "cu_q[batch] = %d differs from total_q %d", cu_q[batch], total_q);
+    const int g = q_heads / kv_heads;
+    int bq = 0;
+    const int layout = msgl::prefill_layout(batch, total_q, g, &bq);
+    struct Entry {
+        int32_t tiles, b, qb;
+    };
+    std::vector<Entry> list;
+    for (int32_t b = 0; b < batch; ++b) {
+        const int64_t e = (int64_t)cu_q[b + 1] - cu_q[b];
+        const int64_t c = cached_lens[b];
+        if (e < 1 || c < 0 || c + e != seq_lens[b])
+            return fail(MSGL_INVALID_ARG, "request %d: cu_q step %lld, cached %lld, seq_len %d (need step >= 1 and "
+                        "cached + step == seq_len)", b, (long long)e, (long long)c, seq_lens[b]);
+        if (seq_lens[b] > row_stride)
+            return fail(MSGL_INVALID_ARG, "request %d: seq_len %d exceeds row_stride %d", b, seq_lens[b], row_stride);
+        if (table_idx[b] < 0 || table_idx[b] >= rows)
+            return fail(MSGL_INVALID_ARG, "request %d: table row %d not in [0, %d)", b, table_idx[b], rows);
+        for (int64_t qb = 0; qb * bq < e; ++qb) {
+            const int64_t keys = c + std::min<int64_t>((qb + 1) * bq, e);
+            list.push_back({(int32_t)((keys + msgl::kPlanKeyTile - 1) / msgl::kPlanKeyTile), b, (int32_t)qb});
+        }
+    }
+    const size_t need = (msgl::kPlanHeaderInts + list.size() * (size_t)msgl::kPlanEntryInts) * sizeof(int32_t);
+    if (plan_bytes < need) return fail(MSGL_WORKSPACE_TOO_SMALL, "plan buffer %zu bytes < %zu required", plan_bytes, need);
+    std::stable_sort(list.begin(), list.end(), [](const Entry &x, const Entry &y) { return x.tiles > y.tiles; });
+    const int32_t head[msgl::kPlanHeaderInts] = {msgl::kPlanMagic, layout, bq, (int32_t)list.size(),
+                                                 batch, total_q, q_heads, kv_heads};
+    for (int i = 0; i < msgl::kPlanHeaderInts; ++i) plan[i] = head[i];
+    int32_t *e = plan + msgl::kPlanHeaderInts;
+    for (const Entry &x : list) {
+        const int32_t ent[msgl::kPlanEntryInts] = {x.b, x.qb, cu_q[x.b + 1] - cu_q[x.b], cached_lens[x.b],
+                                                   cu_q[x.b], table_idx[x.b], x.tiles, 0};
+        for (int i = 0; i < msgl::kPlanEntryInts; ++i) e[i] = ent[i];
+        e += msgl::kPlanEntryInts;
+    }
+    return ok();
+}
+
+msgl_status msgl_prefill_attn_planned(void *out, float *lse, const void *q, const void *k_pool,
+                                      const void *v_pool, int64_t num_slots, const int32_t *page_table,
+                                      int32_t row_stride, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                      int32_t page_size, float sm_scale, msgl_dtype dtype,
+                                      const int32_t *plan_host, const int32_t *plan_dev, size_t plan_bytes,
+                                      void *stream) {
+    if (dtype != MSGL_BF16 || head_dim != 128)
+        return fail(MSGL_UNSUPPORTED, "the planned prefill runs the bf16 matrix-core kernels (head_dim 128)");
+    msgl_status s = check_common(dtype, head_dim, kv_heads, num_slots);
+    if (s != MSGL_OK) return s;
+    if ((s = check_group(q_heads, kv_heads)) != MSGL_OK) return s;
+    if (!plan_host || !plan_dev) return fail(MSGL_INVALID_ARG, "NULL plan");
+    if (plan_bytes < msgl::kPlanHeaderInts * sizeof(int32_t) || plan_host[0] != msgl::kPlanMagic)
+        return fail(MSGL_INVALID_ARG, "not a prefill plan (bad header)");
+    const int32_t layout = plan_host[1], bq = plan_host[2], entries = plan_host[3];
+    const int32_t batch = plan_host[4], total_q = plan_host[5];
+    int want_bq = 0;
+    const int want_layout = msgl::prefill_layout(batch, total_q, q_heads / kv_heads, &want_bq);
+    if (plan_host[6] != q_heads || plan_host[7] != kv_heads || layout != want_layout || bq != want_bq ||
+        entries < 0 || batch < 0 || total_q < 0)
+        return fail(MSGL_INVALID_ARG, "the plan was made for other heads or is malformed (layout %d, %d tokens per "
+                    "block, %d entries)", layout, bq, entries);
+    if (plan_bytes < (msgl::kPlanHeaderInts + (size_t)entries * msgl::kPlanEntryInts) * sizeof(int32_t))
+        return fail(MSGL_INVALID_ARG, "plan_bytes %zu too small for %d entries", plan_bytes, entries);
+    if (entries == 0) return ok();
+    if (!out || !q || !k_pool || !v_pool || !page_table) return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    if (row_stride < 1) return fail(MSGL_INVALID_ARG, "row_stride %d < 1", row_stride);
+    if (page_size < 1) return fail(MSGL_INVALID_ARG, "page_size %d < 1", page_size);
+    msgl::PrefillArgs a{};
+    a.out = out;
+    a.lse = lse;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.page_table = page_table;
+    a.row_stride = row_stride;
+    a.num_slots = num_slots;
+    a.batch = batch;
+    a.total_q = total_q;
+    a.max_extend = 0;
+    a.q_heads = q_heads;
+    a.kv_heads = kv_heads;
+    a.scale_log2 = sm_scale * msgl::kLog2eHost;
+    a.splits = 1;
+    a.plan = plan_dev + msgl::kPlanHeaderInts;
+    return from_hip(msgl::launch_prefill_planned(a, layout, entries, static_cast<hipStream_t>(stream)),
+                    "planned prefill launch");
 }
 
 msgl_status msgl_decode_graph_create(msgl_graph **graph, void *k_pool, void *v_pool,

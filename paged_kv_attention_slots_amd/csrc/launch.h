@@ -122,7 +122,24 @@ struct PrefillArgs {
     int32_t splits;
     float *part_o;
     float *part_lse;
+    // planned launches only: the host plan's block list (kPlanEntryInts int32
+    // per entry, device memory); null otherwise
+    const int32_t *plan;
 };
+
+// Host plan of a prefill launch: a header of kPlanHeaderInts int32, then one
+// entry of kPlanEntryInts int32 per query block, in launch order.
+constexpr int32_t kPlanMagic = 0x4d504c31;  // "MPL1"
+constexpr int kPlanHeaderInts = 8;           // magic, layout, query tokens per block, entries, batch, total_q, q_heads, kv_heads
+constexpr int kPlanKeyTile = 64;            // keys per tile of the MFMA kernels (orders the entries)
+constexpr int kPlanEntryInts = 8;            // request, query block, new tokens, cached tokens, first q row, table row, key tiles, 0
+// Layout of the bf16 MFMA prefill kernels for a batch: 1 = the single-block
+// long-chunk layout, 0 = two blocks per CU; *bq receives its query tokens per
+// block for q_heads / kv_heads = group.
+int prefill_layout(int64_t batch, int64_t total_q, int group, int *bq);
+// Query tokens per block of the two-blocks-per-CU layout (the smaller one).
+int prefill_small_bq(int group);
+hipError_t launch_prefill_planned(const PrefillArgs &a, int layout, int entries, hipStream_t stream);
 
 size_t decode_workspace_bytes(int batch, int q_heads, int head_dim, int max_seq_len, int chunk);
 

@@ -74,6 +74,7 @@ constexpr int kIdSlots = 4;                      // page-table id slots per wave
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kMaxBatch = 1024;                  // requests per call on the MFMA path
 }  // namespace pf
+static_assert(pf::kKT == kPlanKeyTile, "the host plan orders blocks by this kernel's key tiles");
 
 namespace pfc {  // two blocks per CU: 4 waves, K and V rings of two tiles each
 constexpr int kWaves = 4;
@@ -332,7 +333,13 @@ MSGL_DEV BlockItem sorted_block(const PrefillArgs &a, int r, int lane) {
     return {-1, 0, 0, 0, 0, 0};
 }
 
-template <int GQ>
+// A block's work item read from the host plan (entry i of its block list).
+MSGL_DEV BlockItem planned_block(const PrefillArgs &a, int i) {
+    const int32_t *e = a.plan + (int64_t)i * kPlanEntryInts;
+    return {e[0], e[1], e[2], e[3], e[4], e[5]};
+}
+
+template <int GQ, bool PL = false>
 __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(PrefillArgs a) {
     constexpr int BQ = pfl::kCols / GQ;  // query tokens per block
     constexpr int S = pfl::kStages;
@@ -346,7 +353,8 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 
     // block id = list entry * G + kv head: the query blocks longest first, no gaps
     const int kvh = blockIdx.x % G;
-    const BlockItem item = a.batch <= 64    ? sorted_block<BQ, 1>(a, blockIdx.x / G, lane)
+    const BlockItem item = PL                ? planned_block(a, blockIdx.x / G)
+                           : a.batch <= 64  ? sorted_block<BQ, 1>(a, blockIdx.x / G, lane)
                            : a.batch <= 256 ? sorted_block<BQ, 4>(a, blockIdx.x / G, lane)
                                             : sorted_block<BQ, pf::kMaxBatch / 64>(a, blockIdx.x / G, lane);
     const int b = __builtin_amdgcn_readfirstlane(item.b);
@@ -356,9 +364,10 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
     const int E = __builtin_amdgcn_readfirstlane(item.E);
     const int t0 = qb * BQ;
     if (qb < 0 || C < 0 || t0 >= E) return;
+    if (PL && (int64_t)C + E > a.row_stride) return;  // an entry whose keys pass the table row runs nothing
     const int row0 = __builtin_amdgcn_readfirstlane(item.q0) + t0;
     const int ntok = min(min(BQ, E - t0), a.total_q - row0);
-    if (ntok <= 0) return;
+    if (ntok <= 0 || row0 < 0) return;
     const int pos0 = C + t0;         // position of the block's first token
     const int nkeys = pos0 + ntok;   // keys 0 .. position of its last token
     const int ntiles = (nkeys + pf::kKT - 1) / pf::kKT;
@@ -611,7 +620,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 // group's queries to split s of the shared prefix (no causal mask: every
 // query sits after the prefix) and writes the normalised partial output and
 // its lse, in float32, to split s of the partial arrays.
-template <int GQ, bool SH = false>
+template <int GQ, bool SH = false, bool PL = false>
 __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
     constexpr int BQ = pfc::kCols / GQ;  // query tokens per block
     __shared__ __attribute__((aligned(1024))) char smem[pfc::kLds];
@@ -627,7 +636,8 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int split = SH ? (int)(blockIdx.x % a.splits) : 0;
     const int bid = SH ? (int)(blockIdx.x / a.splits) : (int)blockIdx.x;
     const int kvh = bid % G;
-    const BlockItem item = a.batch <= 64    ? sorted_block<BQ, 1, SH>(a, bid / G, lane)
+    const BlockItem item = PL                ? planned_block(a, bid / G)
+                           : a.batch <= 64  ? sorted_block<BQ, 1, SH>(a, bid / G, lane)
                            : a.batch <= 256 ? sorted_block<BQ, 4, SH>(a, bid / G, lane)
                                             : sorted_block<BQ, pf::kMaxBatch / 64, SH>(a, bid / G, lane);
     const int b = __builtin_amdgcn_readfirstlane(item.b);
@@ -637,6 +647,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int E = __builtin_amdgcn_readfirstlane(item.E);
     const int t0 = qb * BQ;
     if (qb < 0 || C < 0 || t0 >= E) return;
+    if (PL && (int64_t)C + E > a.row_stride) return;  // an entry whose keys pass the table row runs nothing
     const int row0 = __builtin_amdgcn_readfirstlane(item.q0) + t0;
     const int ntok = min(min(BQ, E - t0), a.total_q - row0);
     if (ntok <= 0 || row0 < 0) return;
@@ -909,12 +920,8 @@ int64_t prefill_blocks(const PrefillArgs &a, int BQ) {
 
 template <int GQ>
 hipError_t run_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
-    // Requests of 2048 or more new tokens on average: long, uniform blocks,
-    // where the single-block layout's deeper ring keeps the matrix cores
-    // busier; otherwise block starts and the spread of block lengths weigh
-    // more, and two blocks per CU hide them.
-    const bool long_chunks = (int64_t)a.total_q >= 2048 * (int64_t)a.batch;
-    const int BQ = (long_chunks ? pfl::kCols : pfc::kCols) / GQ;
+    int BQ = 0;
+    const bool long_chunks = prefill_layout(a.batch, a.total_q, GQ, &BQ) == 1;
     const int64_t grid = prefill_blocks(a, BQ);
     if (grid < 1) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
@@ -925,7 +932,44 @@ hipError_t run_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int GQ>
+hipError_t run_prefill_planned(const PrefillArgs &a, int layout, int entries, hipStream_t stream) {
+    const int64_t grid = (int64_t)entries * a.kv_heads;
+    if (grid < 1) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (layout == 1)
+        hipLaunchKernelGGL((prefill_mfma_long_kernel<GQ, true>), dim3((unsigned)grid), dim3(pfl::kThreads), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL((prefill_mfma_kernel<GQ, false, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+// Requests of 2048 or more new tokens on average: long, uniform blocks, where
+// the single-block layout's deeper ring keeps the matrix cores busier;
+// otherwise block starts and the spread of block lengths weigh more, and two
+// blocks per CU hide them.
+int prefill_layout(int64_t batch, int64_t total_q, int group, int *bq) {
+    const bool long_chunks = total_q >= 2048 * batch;
+    if (bq != nullptr) *bq = (long_chunks ? pfl::kCols : pfc::kCols) / (group > 0 ? group : 1);
+    return long_chunks ? 1 : 0;
+}
+
+int prefill_small_bq(int group) { return pfc::kCols / (group > 0 ? group : 1); }
+
+hipError_t launch_prefill_planned(const PrefillArgs &a, int layout, int entries, hipStream_t stream) {
+    if (a.plan == nullptr || (layout != 0 && layout != 1) || entries < 0) return hipErrorInvalidValue;
+    switch (a.q_heads / a.kv_heads) {
+        case 1: return run_prefill_planned<1>(a, layout, entries, stream);
+        case 2: return run_prefill_planned<2>(a, layout, entries, stream);
+        case 4: return run_prefill_planned<4>(a, layout, entries, stream);
+        case 8: return run_prefill_planned<8>(a, layout, entries, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_prefill_shared(const PrefillArgs &a, hipStream_t stream) {
     if (a.batch > pf::kMaxBatch || a.splits < 1) return hipErrorInvalidValue;

@@ -139,6 +139,7 @@ hipError_t launch_decode_shared_prefix(const SharedPrefixArgs &sp, const DecodeA
         p.splits = splits;
         p.part_o = prefix_o;
         p.part_lse = prefix_lse;
+        p.plan = nullptr;
         hipError_t e = launch_prefill_shared(p, stream);
         if (e != hipSuccess) return e;
     }

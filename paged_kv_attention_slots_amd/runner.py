@@ -55,6 +55,28 @@ def prefill_attn(w: Workload, k_pool, v_pool, out=None, lse=None, with_lse: bool
     return out, lse
 
 
+def prefill_plan(w: Workload):
+    """The host plan of w's prefill launch: (host int32 tensor, its device copy)."""
+    plan = _lib.msgl_prefill_plan(w.seq_lens.cpu(), w.cached_lens.cpu(), w.cu_q.cpu(), w.table_idx.cpu(),
+                                  w.page_table.shape[0], w.page_table.shape[1], w.q_heads, w.kv_heads,
+                                  w.head_dim, _lib._dt(w.q))
+    return plan, plan.to(w.q.device)
+
+
+def prefill_attn_planned(w: Workload, k_pool, v_pool, plan=None, out=None, lse=None, with_lse: bool = True,
+                         stream=None):
+    dev = w.q.device
+    if plan is None:
+        plan = prefill_plan(w)
+    if out is None:
+        out = torch.empty_like(w.q)
+    if lse is None and with_lse:
+        lse = torch.empty(w.num_tokens, w.q_heads, dtype=torch.float32, device=dev)
+    _lib.msgl_prefill_attn_planned(out, lse, w.q, k_pool, v_pool, w.page_table, plan[0], plan[1],
+                                   page_size=w.page_size, sm_scale=w.sm_scale, stream=stream)
+    return out, lse
+
+
 def run_step(w: Workload, chunk: int = 0, with_lse: bool = True, in_place: bool = False) -> StepResult:
     """store_kv then attention (decode or prefill by the workload's mode)."""
     kp = w.k_pool if in_place else w.k_pool.clone()
