@@ -229,8 +229,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     // piece k of this request (block first + k) keeps its state at index (b + first + k) * q_heads + h
     const int64_t i0 = ((int64_t)b + first) * a.q_heads + h;
     const int64_t pstride = (int64_t)a.q_heads * D;  // floats between consecutive pieces' outputs
-    float mx = -INFINITY;
-    for (int k = lane; k < n; k += 64) mx = fmaxf(mx, a.part_ml[(i0 + (int64_t)k * a.q_heads) * 2]);
+    // (max, sum) of the lane's first piece, kept for the weights below
+    float m0 = -INFINITY, l0 = 0.0f;
+    if (lane < n) {
+        const float2 v = *reinterpret_cast<const float2 *>(a.part_ml + (i0 + (int64_t)lane * a.q_heads) * 2);
+        m0 = v.x;
+        l0 = v.y;
+    }
+    float mx = m0;
+    for (int k = lane + 64; k < n; k += 64) mx = fmaxf(mx, a.part_ml[(i0 + (int64_t)k * a.q_heads) * 2]);
     mx = wave_max64(mx);
     float l = 0.0f;
     float acc[DPL];
@@ -240,9 +247,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         const int k = c0 + lane;
         float wk = 0.0f;
         if (k < n) {
-            const int64_t idx = i0 + (int64_t)k * a.q_heads;
-            wk = fast_exp2(a.part_ml[idx * 2] - mx);
-            l = fmaf(a.part_ml[idx * 2 + 1], wk, l);
+            float mk = m0, lk = l0;
+            if (c0 != 0) {
+                const float2 v = *reinterpret_cast<const float2 *>(a.part_ml + (i0 + (int64_t)k * a.q_heads) * 2);
+                mk = v.x;
+                lk = v.y;
+            }
+            wk = fast_exp2(mk - mx);
+            l = fmaf(lk, wk, l);
         }
         const int cn = min(64, n - c0);
         const float *po = a.part_o + i0 * D + (int64_t)c0 * pstride + col;
