@@ -100,6 +100,7 @@ def rope_store_bytes(w) -> int:
 
 ROPE_BASE = 1e6  # Qwen3's rotary base
 PREFILL_WARM_LAUNCHES = 400  # ~40 ms of the ragged prefill kernel before it is timed alone
+KERNEL_ITERS = 20  # default number of eager decode-attention launches timed for the roofline
 
 
 def prefill_flops(w) -> float:
@@ -163,6 +164,17 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes,
     lines += ["## library kernels, whole run", head] + [row(r) for r in mine]
     lines += ["", "## the decode step (Qwen3-8B bs 256: graph replays, then eager launches) and the ragged prefill",
               head] + legs(True)
+    # the roofline's kernel: the eager decode-attention launches the bench line times (the
+    # last KERNEL_ITERS split + merge pairs before the cut) against its HIP-event average
+    def eager(kind):
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+             if kind in r["Kernel_Name"] and int(r["Dispatch_Id"]) < cut]
+        return d[-KERNEL_ITERS:]
+    sp, mg = eager("decode_split_kernel"), eager("decode_merge_kernel")
+    if sp and mg:
+        lines += ["", f"## the roofline's kernel: the {len(sp)} eager decode-attention launches the bench line times",
+                  f"split {sum(sp) / len(sp):.2f} us + merge {sum(mg) / len(mg):.2f} us = "
+                  f"{sum(sp) / len(sp) + sum(mg) / len(mg):.2f} us per launch"]
     lines += ["", "## after them: fused RoPE (decode and prefill batches), vocabulary indexing (4288 and 256 tokens),",
               "## shared-prefix batch (cascade call: prefix MFMA pass, suffix decode, merge; then plain decode)",
               head] + legs(False)
@@ -584,7 +596,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--page-size", type=int, default=1, choices=(1, 16))
     ap.add_argument("--chunk", type=int, default=0, help="decode split size (0 = library default)")
-    ap.add_argument("--kernel-iters", type=int, default=20, help="eager decode launches timed for the roofline")
+    ap.add_argument("--kernel-iters", type=int, default=KERNEL_ITERS, help="eager decode launches timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-reqs", type=int, default=256,
                     help="decode requests the CPU oracle is timed on (first N of the batch)")
