@@ -227,8 +227,9 @@ msgl_status msgl_prefill_attn(void *out, float *lse, const void *q, const void *
                               msgl_dtype dtype, void *stream);
 
 /*
- * Host plan / run split of the prefill call, after the plan-then-run structure
- * of the FlashInfer backend that the Stage 4 milestone's engine uses: the
+ * Host plan / run split of the prefill call, after the plan and run steps of
+ * the FlashInfer attention backend ("Stage 4 milestone": the table 'What each
+ * chapter adds' and the stage checkpoint, which asks what each step does): the
  * block list that msgl_prefill_attn derives on the device from the lengths
  * (every (request, query block) pair, the most key tiles first, ties in
  * request order, one launch block per entry and kv head) is made on the host
