@@ -5,6 +5,7 @@ msgl_prefill_attn's bit for bit; against the fp64 oracle they meet the bf16
 bar.  A batch beyond the 1024 requests of the device enumeration runs on the
 matrix cores only when planned."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -100,3 +101,26 @@ def test_planned_beyond_device_enumeration(oracle_mod, runner, wl):
     say(f"[plan] {w.bs} requests, sampled {len(rows)} rows: max-abs {err:.3e}")
     assert err <= tol(w), err
     assert max_abs(lse[idx], lse_ref) < 1e-3
+
+
+def test_planned_single_new_tokens_and_full_row(runner, wl):
+    # one-token extends, tile-edge lengths, and a request whose keys fill its whole 32768-entry row
+    cached = [0, 5, 32700, 0, 63, 64]
+    ext = [1, 1, 68, 130, 1, 65]
+    lens = [c + e for c, e in zip(cached, ext)]
+    rng = np.random.default_rng(79)
+    rows = wl.rows_from_free_slots(rng.permutation(1 << 16), lens, new_after_history=False)
+    w = wl.build_workload("prefill-edges", "prefill", torch.bfloat16, **wl.QWEN3_06B, page_size=1,
+                          num_slots=1 << 16, max_running_req=len(lens), max_seq_len=32768, rows=rows,
+                          seq_lens=lens, cached_lens=cached, seed=79, q_std=1.0, device="cuda")
+    assert max(lens) == w.row_stride
+    _same_as_unplanned(runner, w)
+
+
+def test_planned_long_layout_page16(runner, wl):
+    # the single-block layout over shuffled 16-token pages
+    w = wl.ragged_prefill(device="cuda", n_req=2, e_lo=2100, e_hi=2600, c_lo=300, c_hi=3000, num_slots=1 << 14,
+                          seed=68, page_size=16, heads=dict(H=16, G=8, d=128))
+    plan = runner.prefill_plan(w)
+    assert int(plan[0][1]) == 1
+    _same_as_unplanned(runner, w)
