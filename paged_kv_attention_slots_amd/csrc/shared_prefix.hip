@@ -38,32 +38,56 @@ struct CascadeMergeArgs {
     int32_t splits;             // 0 when the prefix pass did not run
 };
 
-// One wave per (request, q head); each lane owns D / 64 elements.
+namespace {
+
+MSGL_DEV float lanes_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+MSGL_DEV float lanes_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+}  // namespace
+
+// One wave per (request, q head); each lane owns D / 64 elements.  Lane s
+// reads split s's lse, so the weights take one round trip; the splits' partial
+// outputs are then read with every split's loads in flight at once (the loop
+// over kMaxPrefixSplits is unrolled).  An empty split (lse = -inf) was never
+// written and is skipped.
 template <int D>
 __global__ __launch_bounds__(256) void cascade_merge_kernel(CascadeMergeArgs a) {
     constexpr int PER = D / 64;
+    static_assert(kMaxPrefixSplits <= 64, "one lane per split");
     const int b = blockIdx.x;
     const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (h >= a.q_heads) return;
     const int64_t bh = (int64_t)b * a.q_heads + h;
-    const int S = a.prefix_lens[b] > 0 ? a.splits : 0;
+    const int S = a.prefix_lens[b] > 0 ? min(a.splits, kMaxPrefixSplits) : 0;
     const int64_t sstride = (int64_t)a.batch * a.q_heads;
-    float m = a.suffix_lse[bh];
-    for (int s = 0; s < S; ++s) m = fmaxf(m, a.prefix_lse[s * sstride + bh]);
-    float w = expf(a.suffix_lse[bh] - m);
-    float l = w;
+    const float xs = a.suffix_lse[bh];
+    const float x = lane < S ? a.prefix_lse[lane * sstride + bh] : -INFINITY;
+    const float m = fmaxf(lanes_max(x), xs);
+    const float wx = x == -INFINITY ? 0.0f : expf(x - m);
+    const float ws = expf(xs - m);
+    const float l = lanes_sum(wx) + ws;
+    const uint64_t live = __ballot(x != -INFINITY);
     float acc[PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = w * a.suffix_o[bh * D + lane * PER + e];
-    for (int s = 0; s < S; ++s) {
-        const float x = a.prefix_lse[s * sstride + bh];
-        if (x == -INFINITY) continue;  // an empty split (its partial output was never written)
-        w = expf(x - m);
-        l += w;
-        const float *po = a.prefix_o + (s * sstride + bh) * D + lane * PER;
+    for (int e = 0; e < PER; ++e) acc[e] = ws * a.suffix_o[bh * D + lane * PER + e];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[e], acc[e]);
+    for (int s = 0; s < kMaxPrefixSplits; ++s) {
+        const float w = __shfl(wx, s);
+        if ((live >> s) & 1) {
+            const float *po = a.prefix_o + (s * sstride + bh) * D + lane * PER;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[e], acc[e]);
+        }
     }
     const float inv = 1.0f / l;
     bf16_t *op = a.out + bh * D + lane * PER;
