@@ -101,6 +101,7 @@ def rope_store_bytes(w) -> int:
 ROPE_BASE = 1e6  # Qwen3's rotary base
 PREFILL_WARM_LAUNCHES = 400  # ~40 ms of the ragged prefill kernel before it is timed alone
 KERNEL_ITERS = 20  # default number of eager decode-attention launches timed for the roofline
+SETTLE_STEPS = 60  # untimed full steps before the warm-up steps (~45 ms of GPU work)
 
 
 def prefill_flops(w) -> float:
@@ -651,8 +652,11 @@ def main() -> int:
                                w3.seq_lens, w3.cached_lens, w3.cu_q, max_ext3, page_size=w3.page_size,
                                sm_scale=w3.sm_scale, stream=stream)
 
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
+    # settle: the first few tens of steps after matrix work starts run the decode leg 10-15%
+    # slower (a start-up transient of the clocks or power state: it is gone after ~50 steps
+    # and does not come back); full steps, untimed, before the W warm-up steps
+    log(f"settle {SETTLE_STEPS} steps, warmup {args.warmup} steps")
+    for _ in range(SETTLE_STEPS + args.warmup):
         graph.launch(stream)
         prefill_leg()
     torch.cuda.synchronize()
@@ -840,6 +844,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_steps": SETTLE_STEPS,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
