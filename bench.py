@@ -503,7 +503,7 @@ def mixed(iters: int) -> int:
             _lib.msgl_prefill_attn(op, None, p.q, p.k_pool, p.v_pool, p.page_table, p.table_idx, p.seq_lens,
                                    p.cached_lens, p.cu_q, max_ext, stream=stream)
 
-    ms = _time_stream(step, stream, iters, warm=2)
+    ms = _time_stream(step, stream, iters, warm=4)  # past the start-up transient of matrix work
     dbytes = decode_bytes(d0) * m.layers
     sbytes = (2 * 2 * m.num_tokens * d0.kv_heads * d0.head_dim * 2 + 4 * m.num_tokens) * m.layers
     flops = prefill_flops(p0) * m.layers
