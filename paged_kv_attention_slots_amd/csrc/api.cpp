@@ -1,6 +1,7 @@
 // C ABI of libmsgl (declared in include/msgl.h): argument checks, dispatch to
-// the kernel launchers, decode-step graph capture, and the host-side batch
-// validator.  Nothing here allocates device memory or synchronises.
+// the kernel launchers, decode-step graph capture, the host-side batch
+// validators and the prefill launch's host plan.  Nothing here allocates
+// device memory or synchronises.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
