@@ -42,7 +42,11 @@
  * Preconditions on device-array contents are not checked by the compute calls
  * (checking them would need a host synchronisation); msgl_validate_batch
  * checks host copies.  Only host scalars and pointer presence are validated;
- * a bad value returns a status and enqueues nothing.
+ * a bad value returns a status and enqueues nothing.  The kernels clamp the
+ * slot ids and lengths they read into range, but table_idx is a pure
+ * precondition (0 <= table_idx[b] < the page table's rows, a count the
+ * attention calls do not receive): an id out of range reads outside the
+ * page table.
  *
  * Supported: dtype F32 or BF16; head_dim 64 or 128; q_heads / kv_heads in
  * {1, 2, 4, 8}; kv_heads <= 64; page_size >= 1.  Others return
@@ -139,6 +143,12 @@ msgl_status msgl_vocab_embed(void *out, const void *weight, int64_t vocab_start,
  * Decode attention: one query token per request, at position seq_lens[b] - 1
  * (the token just written by msgl_store_kv, so a request attends to itself).
  * The keys of request b are page_table[table_idx[b], 0 .. seq_lens[b]-1].
+ * Defined by: "mini-sglang from Scratch, Engine and sampler" (the page-table
+ * section: one row per request holding each token's KV location; the
+ * hand-driven decode step: positions cached_len .. device_len - 1 and out_loc
+ * the row's entries there) and the Mini-SGLang tag page's KV-cache article
+ * (section 1: the query of step t attends the keys and values of positions
+ * 0..t) and Engine article (section 1: the KV write precedes attention).
  *
  * The key sequences of all requests, laid end to end (each request counted as
  * its keys plus a fixed cost of 32 key-equivalents, so runs of very short
@@ -152,7 +162,9 @@ msgl_status msgl_vocab_embed(void *out, const void *weight, int64_t vocab_start,
  * once serves any batch whose lengths stay within it).
  *
  * msgl_decode_workspace_bytes returns the workspace size for these scalars.
- * seq_lens[b] must lie in [1, min(max_seq_len, row_stride)].
+ * seq_lens[b] must lie in [1, min(max_seq_len, row_stride)].  Calls with
+ * batch * (max_seq_len + 32) >= 2^31 return MSGL_UNSUPPORTED (the split
+ * counts work units in 32 bits).
  */
 size_t msgl_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim,
                                    int32_t max_seq_len, int32_t chunk);
@@ -211,10 +223,17 @@ msgl_status msgl_decode_attn_shared_prefix(void *out, float *lse, const void *q,
  * already in the pool from earlier steps; its new tokens are q rows
  * cu_q[b] .. cu_q[b+1]-1 at positions cached_lens[b] .. seq_lens[b]-1, and
  * each sees the keys at positions 0..its own position (the causal mask is
- * offset by the cached length).  Requires
+ * offset by the cached length).  Defined by: "mini-sglang from Scratch,
+ * Engine and sampler" (the hand-driven prefill: positions from cached_len to
+ * device_len, a batch of several requests concatenated), the Mini-SGLang tag
+ * page's KV-cache article (section 1: the query at position t attends
+ * positions 0..t; the radix prefix cache supplies the cached prefix) and its
+ * scheduler article (chunked prefill: a request's prompt may arrive in
+ * pieces on top of what is cached).  Requires
  * cu_q[b+1] - cu_q[b] == seq_lens[b] - cached_lens[b] >= 1, cu_q[0] == 0,
- * cu_q[batch] == total_q, and max_extend >= every extend length (it sizes
- * the grid).  bf16 runs on matrix cores (MFMA); fp32 runs on the vector ALUs.
+ * cu_q[batch] == total_q, and max_extend in [1, total_q] (the longest extend
+ * length; the grid is sized from total_q, so an understated value changes
+ * nothing).  bf16 runs on matrix cores (MFMA); fp32 runs on the vector ALUs.
  * The prefill call needs no workspace.
  */
 msgl_status msgl_prefill_attn(void *out, float *lse, const void *q, const void *k_pool,

@@ -76,6 +76,9 @@ msgl_status check_decode(const void *out, const void *q, const void *k_pool, con
     if (max_seq_len < 1 || max_seq_len > row_stride)
         return fail(MSGL_INVALID_ARG, "max_seq_len %d not in [1, row_stride=%d]", max_seq_len, row_stride);
     if (page_size < 1) return fail(MSGL_INVALID_ARG, "page_size %d < 1", page_size);
+    // the split's running count of work units (keys + 32 per request) is int32
+    if ((int64_t)batch * ((int64_t)max_seq_len + 32) >= ((int64_t)1 << 31))
+        return fail(MSGL_UNSUPPORTED, "batch %d x (max_seq_len %d + 32) work units reach 2^31", batch, max_seq_len);
     const int32_t c = effective_chunk(chunk);
     if (c < 64 || c % 64 != 0) return fail(MSGL_INVALID_ARG, "chunk %d is not a positive multiple of 64", chunk);
     const size_t need = msgl::decode_workspace_bytes(batch, q_heads, head_dim, max_seq_len, c);

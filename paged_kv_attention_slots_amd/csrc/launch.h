@@ -123,8 +123,9 @@ struct PrefillArgs {
     float *part_o;
     float *part_lse;
     // planned launches only: the host plan's block list (kPlanEntryInts int32
-    // per entry, device memory); null otherwise
+    // per entry, device memory) and its entry count; null / 0 otherwise
     const int32_t *plan;
+    int32_t plan_entries;
 };
 
 // Host plan of a prefill launch: a header of kPlanHeaderInts int32, then one

@@ -45,10 +45,13 @@
 // Softmax: log2 domain (scale times log2 e folded into one fma before exp2),
 // one running max per column per unit and lazy rescaling: the max only moves
 // when a unit's max exceeds it by more than 2^8, which keeps exp2 arguments
-// bounded and skips almost every rescale.  One fp32 sum of the unrounded
-// weights, lane-partial and reduced once at the end, gives both the
-// normalisation and the returned lse.  The P.V product uses the weights
-// rounded to bf16, so the applied weights sum to one within 2^-9 relative.
+// bounded and skips almost every rescale.  The P.V product applies the
+// weights rounded to bf16, so the output is normalised by the fp32 sum of
+// those rounded weights (a v_dot2 with a pair of ones per pair): the applied
+// weights then sum to one up to float32 rounding (V = 1 gives exactly 1),
+// whatever the size of the weights.  The returned lse comes from a second
+// fp32 sum, of the unrounded weights.  Both sums are lane-partial and are
+// reduced once at the end.
 //
 // Block ids enumerate the query blocks of all requests densely, in decreasing
 // order of the keys they see (computed in the kernel from the lengths), so the
@@ -74,6 +77,10 @@ constexpr int kIdSlots = 4;                      // page-table id slots per wave
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kMaxBatch = 1024;                  // requests per call on the MFMA path
 }  // namespace pf
+// Two bf16 ones (v_dot2 with it sums a pair of weights).
+constexpr uint32_t kBf16OnesPair = 0x3f803f80u;
+// A unit whose weights exceed this somewhere raises the softmax reference (2^64).
+constexpr float kPrefillWeightBound = 18446744073709551616.0f;
 static_assert(pf::kKT == kPlanKeyTile, "the host plan orders blocks by this kernel's key tiles");
 
 namespace pfc {  // two blocks per CU: 4 waves, K and V rings of two tiles each
@@ -85,8 +92,8 @@ constexpr int kVBase = 2 * pf::kTile;            // V ring
 constexpr int kIdsBase = 4 * pf::kTile;          // per wave, kIdSlots tiles of ids
 constexpr int kLds = kIdsBase + kWaves * pf::kIdSlots * pf::kKT * 4;
 constexpr int kRowsW = pf::kKT / kWaves;         // rows of a tile this wave gathers
-constexpr int kGathers = kRowsW / 4;             // ... four per copy instruction
 static_assert(2 * kLds <= 160 * 1024, "two blocks must fit one CU's LDS");
+static_assert(kRowsW == 16, "a wave's gathers of a tile: 4 instructions of 4 rows");
 }  // namespace pfc
 
 namespace pfl {  // long chunks: one block per CU, 8 waves, a ring of 4 tiles
@@ -169,6 +176,12 @@ MSGL_DEV void copy4_to_lds(const void *base, uint32_t lane_off, uint32_t lds) {
 
 MSGL_DEV void copy16_to_lds(const void *src, uint32_t lds) {
     asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// The same with the source as a 32-bit byte offset from a wave-uniform base
+// (pools below 4 GiB): the address is base + off, with no 64-bit arithmetic.
+MSGL_DEV void copy16_to_lds_at(const void *base, uint32_t off, uint32_t lds) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 template <int N>
@@ -459,7 +472,8 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = floatx16_t{};
     float m;                          // running column max (log2 units; may lag by < 2^8)
-    float lt = 0.0f;                  // this lane's share of the running sum of the weights
+    float lt = 0.0f;                  // this lane's share of the running sum of the weights: the lse
+    float lr = 0.0f;                  // ... of the weights rounded to bf16, as P.V applies them: the normalisation
     floatx16_t sc;                    // raw scores of the unit whose softmax is next
     bf16x8_t pb[2];                   // weights of the unit whose P.V is next
 
@@ -486,16 +500,20 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
         mx = fmaxf(mx, s[15]);
         return max_with_other_half(mx) * a.scale_log2;  // raw scores: the scale is positive
     };
-    // weights exp2(s * scale - mu), rounded pairs for P.V, and their sum
-    auto weights = [&](const floatx16_t &s, float mu, bf16x8_t (&out)[2], float &sum) __attribute__((always_inline)) {
+    // weights exp2(s * scale - mu), rounded pairs for P.V, the sum of the
+    // weights and the sum of the rounded weights
+    auto weights = [&](const floatx16_t &s, float mu, bf16x8_t (&out)[2], float &sum, float &rsum)
+                       __attribute__((always_inline)) {
         uint32_t pw[8];
         sum = 0.0f;
+        rsum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, -mu));
             const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, -mu));
             pw[e >> 1] = pack_bf16x2(p0, p1);
             sum += p0 + p1;
+            rsum = dot2_bf16(pw[e >> 1], kBf16OnesPair, rsum);
         }
         out[0] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
         out[1] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
@@ -523,20 +541,21 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
         floatx16_t s_new;
         if (has_scores) s_new = scores(next, half);
         pv(stage, half);
-        float mn = m, lt_u = 0.0f;
+        float mn = m, lt_u = 0.0f, lr_u = 0.0f;
         bf16x8_t pb_new[2];
         if (has_softmax) {
             const float mx = column_max(sc);
             mn = mx > m + pf::kRescaleLog2 ? mx : m;  // lazy: move the max only by more than 2^8
-            weights(sc, mn, pb_new, lt_u);
+            weights(sc, mn, pb_new, lt_u, lr_u);
             // keep the weights in this block (the compiler would otherwise sink
             // them past the rescale branch, away from the MFMAs they overlap)
-            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u));
+            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u), "v"(lr_u));
         }
         if (has_scores && has_softmax) interleave_unit<2, 10, 3, 8>();
         if (has_softmax && __any(mn != m)) {  // rare: rescale what units <= u accumulated
             const float alpha = fast_exp2(m - mn);
             lt *= alpha;
+            lr *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -545,6 +564,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
         if (has_softmax) {
             m = mn;
             lt += lt_u;
+            lr += lr_u;
             pb[0] = pb_new[0];
             pb[1] = pb_new[1];
         }
@@ -573,7 +593,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
         sc = scores(0, 1);
         mask(s0, 0);
         m = column_max(s0);  // key 0 is visible to every column: finite
-        weights(s0, m, pb, lt);
+        weights(s0, m, pb, lt, lr);
     }
     int t = 0;
     for (; t + S <= ntiles - 1; t += S) {
@@ -590,9 +610,12 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
     // the id copies issued past the last tile must land before the block's LDS is released
     wait_vmcnt<0>();
 
+    // normalised by the sum of the weights P.V applied (V = 1 gives 1 exactly);
+    // lse from the sum of the unrounded weights
     lt = add_with_other_half(lt);
+    lr = add_with_other_half(lr);
     if (valid) {
-        const float inv = 1.0f / lt;
+        const float inv = 1.0f / lr;
         bf16_t *op = reinterpret_cast<bf16_t *>(a.out) + ((int64_t)(row0 + tl) * a.q_heads + hq) * pf::kD;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -613,14 +636,28 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 // At tile t the wave waits for all its copies and a barrier makes everyone's
 // visible (K of t+1, V of t, issued in tile t-1, and the ids of t+2 for this
 // tile's gathers); then it refills the stages tile t-1 used, K of t+2 and V of
-// t+1, copies the ids of t+3, and runs units 2t and 2t+1 as above.
+// t+1, copies the ids of t+3, and runs units 2t and 2t+1.
+//
+// Differences from the single-block layout:
+//  - Gathers: wave w's instruction i writes LDS rows 16w + 4i + lane/16, each
+//    the row of key 16w + 4(lane/16) + i of the tile, so a lane's 4 ids are
+//    adjacent (one 16-byte LDS read).  With O32 (pools below 4 GiB) the rows
+//    are addressed as 32-bit offsets from the pool base.
+//  - Each unit runs P.V first, then the scores of the unit two ahead.
+//  - Softmax without a per-unit maximum: the weights are taken against the
+//    first unit's column maximum m.  A unit whose weights pass 2^64 in some
+//    lane (or are not finite) raises m to its own column maximum and rescales
+//    what came before; this branch is rare and, so that none of it runs on
+//    the common path, its inputs go through an opaque copy.
+//  - Each wave stops computing after its last tile (the one holding its last
+//    query's key); it still takes part in every tile's copies and barrier.
 //
 // In shared-prefix mode (SH, decode requests grouped by a shared radix prefix)
 // the block id also carries a key split s < a.splits: the block attends its
 // group's queries to split s of the shared prefix (no causal mask: every
 // query sits after the prefix) and writes the normalised partial output and
 // its lse, in float32, to split s of the partial arrays.
-template <int GQ, bool SH = false, bool PL = false>
+template <int GQ, bool SH, bool PL, bool O32>
 __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
     constexpr int BQ = pfc::kCols / GQ;  // query tokens per block
     __shared__ __attribute__((aligned(1024))) char smem[pfc::kLds];
@@ -629,6 +666,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int jj = lane >> 5;
+    const int grp = lane >> 4;
     const int G = a.kv_heads;
 
     // block id = (list entry * G + kv head) [* splits + split]: the query blocks
@@ -665,6 +703,11 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const bool valid = tl < ntok;
     const int tok = valid ? tl : ntok - 1;
     const int pos = SH ? pos0 : pos0 + tok;
+    // this wave's last tile: the one holding its last valid query's last key (-1: no valid query)
+    const int wfirst = (wave * pf::kColsW) / GQ;
+    const int tw = wfirst >= ntok ? -1
+                   : SH       ? ntiles - 1
+                              : (pos0 + min(ntok - 1, (wave * pf::kColsW + pf::kColsW - 1) / GQ)) / pf::kKT;
 
     if constexpr (SH) {
         if (nkeys <= 0) {  // an empty split: an empty softmax state, marked by lse = -inf
@@ -686,31 +729,27 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     };
     const uint32_t last_slot = (uint32_t)(min(a.num_slots, (int64_t)1 << 31) - 1);
     const uint32_t row_bytes = (uint32_t)G * pf::kRow;
-    const int grp = lane >> 4;
-    const char *kb[pfc::kGathers], *vb[pfc::kGathers];
+    // byte offset, within a pool row, of the chunk lane l loads for gather i (it writes chunk
+    // position l%16 of its LDS row, so it loads the chunk the row permutation puts there)
+    uint32_t lane_off[4];
 #pragma unroll
-    for (int i = 0; i < pfc::kGathers; ++i) {
-        const uint32_t off =
-            (uint32_t)kvh * pf::kRow + (((lane & 15) ^ row_code(pfc::kRowsW * wave + 4 * i + grp)) << 4);
-        kb[i] = reinterpret_cast<const char *>(a.k_pool) + off;
-        vb[i] = reinterpret_cast<const char *>(a.v_pool) + off;
-    }
-    // this wave's rows R*w + 4i + l/16 (i < 4) of the K (or V) rows of tile t,
-    // into ring stage t % 2; lane l writes chunk position l%16 of its row, so
-    // it loads the chunk that the permutation puts there
+    for (int i = 0; i < 4; ++i)
+        lane_off[i] = (uint32_t)kvh * pf::kRow + (((lane & 15) ^ row_code(pfc::kRowsW * wave + 4 * i + grp)) << 4);
+    // gathers of tile t into ring stage t % 2: this wave's 4 instructions
     auto gather = [&](int t, bool is_v) __attribute__((always_inline)) {
-        const uint32_t ids = ids_wave + (t % pf::kIdSlots) * pf::kKT * 4 + (pfc::kRowsW * wave + grp) * 4;
-        const uint32_t base = lds0 + (t & 1) * pf::kTile + (is_v ? pfc::kVBase : pfc::kKBase);
-        int sl[pfc::kGathers];
+        const u32x4_t ids = *(const __attribute__((address_space(3))) u32x4_t *)(uintptr_t)(
+            ids_wave + (t % pf::kIdSlots) * pf::kKT * 4 + (pfc::kRowsW * wave + 4 * grp) * 4);
+        const uint32_t base = lds0 + (t & 1) * pf::kTile + (is_v ? pfc::kVBase : pfc::kKBase) + pfc::kRowsW * wave * pf::kRow;
 #pragma unroll
-        for (int i = 0; i < pfc::kGathers; ++i) {
-            sl[i] = lds_read_i32(ids + 16 * i);
-            sl[i] = (int)min((uint32_t)sl[i], last_slot);  // a malformed id (negative or too large) reads the last slot
-        }
-#pragma unroll
-        for (int i = 0; i < pfc::kGathers; ++i) {
-            const uint32_t dst = base + (pfc::kRowsW * wave + 4 * i) * pf::kRow;
-            copy16_to_lds((is_v ? vb[i] : kb[i]) + (uint64_t)(uint32_t)sl[i] * row_bytes, dst);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t s = min(ids[i], last_slot);  // a malformed id (negative or too large) reads the last slot
+            if constexpr (O32)
+                copy16_to_lds_at(is_v ? a.v_pool : a.k_pool, __umul24(s, row_bytes) + lane_off[i],
+                                 base + 4 * i * pf::kRow);
+            else
+                copy16_to_lds(reinterpret_cast<const char *>(is_v ? a.v_pool : a.k_pool) +
+                                  ((uint64_t)s * row_bytes + lane_off[i]),
+                              base + 4 * i * pf::kRow);
         }
     };
 
@@ -752,8 +791,9 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     floatx16_t acc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = floatx16_t{};
-    float m;
-    float lt = 0.0f;
+    float m;           // reference of the weights (log2 units)
+    float lt = 0.0f;   // lane's share of the sum of the weights: the lse
+    float lr = 0.0f;   // ... of the weights rounded to bf16, as P.V applies them: the normalisation
     floatx16_t sc;
     bf16x8_t pb[2];
 
@@ -764,11 +804,13 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
             s = mfma_32x32x16(lds_read16(kaddr[dc] + stage * pf::kTile + half * 32 * pf::kRow), qv[dc], s);
         return s;
     };
+    // element e of a unit's S^T tile is LDS row 8(e/4) + 4jj + e%4 of the unit, which holds the
+    // unit's key 16(e/8) + 4(e%4) + 2((e/4)%2) + jj (see the gathers)
     auto mask = [&](floatx16_t &s, int u) __attribute__((always_inline)) {
         if (32 * u + 31 > pos0) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int key = 32 * u + 8 * (e >> 2) + 4 * jj + (e & 3);
+                const int key = 32 * u + 16 * (e >> 3) + 4 * (e & 3) + 2 * ((e >> 2) & 1) + jj;
                 s[e] = key > pos ? -INFINITY : s[e];
             }
         }
@@ -780,15 +822,18 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
         mx = fmaxf(mx, s[15]);
         return max_with_other_half(mx) * a.scale_log2;
     };
-    auto weights = [&](const floatx16_t &s, float mu, bf16x8_t (&out)[2], float &sum) __attribute__((always_inline)) {
+    auto weights = [&](const floatx16_t &s, float mu, bf16x8_t (&out)[2], float &sum, float &rsum)
+                       __attribute__((always_inline)) {
         uint32_t pw[8];
         sum = 0.0f;
+        rsum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, -mu));
             const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, -mu));
             pw[e >> 1] = pack_bf16x2(p0, p1);
             sum += p0 + p1;
+            rsum = dot2_bf16(pw[e >> 1], kBf16OnesPair, rsum);
         }
         out[0] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
         out[1] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4], pw[5], pw[6], pw[7]));
@@ -807,79 +852,103 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
                                     pb[1], acc[db]);
         }
     };
+    // One unit: P.V of unit u (tile stage `stage`, half u%2), the scores of
+    // unit u+2 (the same half of the next tile, stage `next`) and the softmax
+    // of unit u+1 (its raw scores are in sc).
     auto unit = [&](int u, int stage, int next, bool has_scores, bool has_softmax) __attribute__((always_inline)) {
         const int half = u & 1;
         if (has_softmax) mask(sc, u + 1);
         floatx16_t s_new;
-        if (has_scores) s_new = scores(next, half);
         pv(stage, half);
-        float mn = m, lt_u = 0.0f;
+        if (has_scores) s_new = scores(next, half);
+        float lt_u = 0.0f, lr_u = 0.0f;
         bf16x8_t pb_new[2];
         if (has_softmax) {
-            const float mx = column_max(sc);
-            mn = mx > m + pf::kRescaleLog2 ? mx : m;
-            weights(sc, mn, pb_new, lt_u);
-            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u));
+            weights(sc, m, pb_new, lt_u, lr_u);
+            // keep the weights in this block (the compiler would otherwise sink
+            // them past the rescale branch, away from the MFMAs they overlap)
+            asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u), "v"(lr_u));
         }
         if (has_scores && has_softmax) interleave_unit<1, 4, 2, 8>();
-        if (has_softmax && __any(mn != m)) {
+        if (has_softmax && __any(!(lt_u <= kPrefillWeightBound))) {  // rare
+            floatx16_t sr = sc;
+            asm volatile("" : "+v"(sr));
+            const float mn = fmaxf(m, column_max(sr));
             const float alpha = fast_exp2(m - mn);
             lt *= alpha;
+            lr *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+            m = mn;
+            weights(sr, m, pb_new, lt_u, lr_u);
         }
         if (has_softmax) {
-            m = mn;
             lt += lt_u;
+            lr += lr_u;
             pb[0] = pb_new[0];
             pb[1] = pb_new[1];
         }
         if (has_scores) sc = s_new;
     };
-    // tile t < ntiles-1 (K of t+1 and V of t were copied in tile t-1): wait for
-    // every copy, then refill the ring stages tile t-1 used with K of t+2 and
-    // V of t+1 and copy the ids of t+3, then units 2t and 2t+1
-    auto tile = [&](int t, int stage) __attribute__((always_inline)) {
+    // start of tile t: wait for this wave's copies, barrier; but at the last
+    // tile, refill the ring stages tile t-1 used with K of t+2 and V of t+1
+    // and copy the ids of t+3
+    auto tile_start = [&](int t) __attribute__((always_inline)) {
         wait_vmcnt<0>();
         lds_barrier();
-        copy_ids(t + 3);  // past the end: a harmless copy of key 0's id
-        if (t + 2 < ntiles) gather(t + 2, false);
-        gather(t + 1, true);
+        if (t < ntiles - 1) {
+            if (t + 3 < ntiles) copy_ids(t + 3);
+            if (t + 2 < ntiles) gather(t + 2, false);
+            gather(t + 1, true);
+        }
+    };
+    auto tile = [&](int t, int stage) __attribute__((always_inline)) {
+        tile_start(t);
         const int next = stage ^ 1;
         unit(2 * t, stage, next, true, true);
         unit(2 * t + 1, stage, next, true, true);
     };
 
     lds_barrier();
-    {
+    if (tw >= 0) {  // scores of units 0 and 1, the first unit's weights against its exact column max
         floatx16_t s0 = scores(0, 0);
         sc = scores(0, 1);
         mask(s0, 0);
-        m = column_max(s0);
-        weights(s0, m, pb, lt);
+        m = column_max(s0);  // key 0 is visible to every column: finite
+        weights(s0, m, pb, lt, lr);
     }
+    // tiles before this wave's last, its last tile, then the block's remaining tiles
     int t = 0;
-    for (; t + 2 <= ntiles - 1; t += 2) {
+    for (; t + 2 <= tw; t += 2) {
         tile(t, 0);
         tile(t + 1, 1);
     }
-    if (t < ntiles - 1) {
+    if (t < tw) {
         tile(t, 0);
         ++t;
     }
-    // the last tile (V of ntiles-1 was copied in the tile before)
-    wait_vmcnt<0>();
-    lds_barrier();
-    const int last = (ntiles - 1) & 1;
-    unit(2 * ntiles - 2, last, 0, false, true);
-    unit(2 * ntiles - 1, last, 0, false, false);
+    if (tw >= 0) {  // this wave's last tile (V of it was copied in the tile before)
+        tile_start(t);
+        if (t & 1) {
+            unit(2 * t, 1, 0, false, true);
+            unit(2 * t + 1, 1, 0, false, false);
+        } else {
+            unit(2 * t, 0, 1, false, true);
+            unit(2 * t + 1, 0, 1, false, false);
+        }
+        ++t;
+    }
+    for (; t < ntiles; ++t) tile_start(t);
 
+    // normalised by the sum of the weights P.V applied (V = 1 gives 1 exactly);
+    // lse from the sum of the unrounded weights
     lt = add_with_other_half(lt);
+    lr = add_with_other_half(lr);
     if constexpr (SH) {
         if (valid) {
-            const float inv = 1.0f / lt;
+            const float inv = 1.0f / lr;
             const int64_t r = ((int64_t)split * a.total_q + row0 + tl) * a.q_heads + hq;
             float *op = a.part_o + r * pf::kD;
 #pragma unroll
@@ -894,7 +963,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
         return;
     }
     if (valid) {
-        const float inv = 1.0f / lt;
+        const float inv = 1.0f / lr;
         bf16_t *op = reinterpret_cast<bf16_t *>(a.out) + ((int64_t)(row0 + tl) * a.q_heads + hq) * pf::kD;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -912,10 +981,30 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
 namespace {
 
 // Query blocks (times the kv heads) of a layout with BQ query tokens per block:
-// at most sum over requests of ceil(E_b / BQ).
+// a bound on the sum over requests of ceil(E_b / BQ) from total_q alone (ids
+// past the real count exit at once), so that no caller-given length can
+// leave query rows without a block.
 int64_t prefill_blocks(const PrefillArgs &a, int BQ) {
-    const int64_t nqb = (a.max_extend + BQ - 1) / BQ;
-    return std::min(nqb * a.batch, ((int64_t)a.total_q + (int64_t)a.batch * (BQ - 1)) / BQ) * a.kv_heads;
+    return ((int64_t)a.total_q + (int64_t)a.batch * (BQ - 1)) / BQ * a.kv_heads;
+}
+
+// Gathers may address pool rows as 32-bit byte offsets from the pool base
+// when every row lies within 4 GiB of it and slot ids fit 24 bits (the
+// offset is a 24-bit multiply).
+bool prefill_o32(const PrefillArgs &a) {
+    const uint64_t row_bytes = (uint64_t)a.kv_heads * pf::kRow;
+    return a.num_slots <= ((int64_t)1 << 24) && (uint64_t)a.num_slots * row_bytes <= ((uint64_t)1 << 32);
+}
+
+// The two-blocks-per-CU kernel with the gather addressing the pool allows.
+template <int GQ, bool SH, bool PL>
+void launch_small(const PrefillArgs &a, int64_t grid, hipStream_t stream) {
+    if (prefill_o32(a))
+        hipLaunchKernelGGL((prefill_mfma_kernel<GQ, SH, PL, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((prefill_mfma_kernel<GQ, SH, PL, false>), dim3((unsigned)grid), dim3(pfc::kThreads), 0,
+                           stream, a);
 }
 
 template <int GQ>
@@ -928,7 +1017,7 @@ hipError_t run_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     if (long_chunks)
         hipLaunchKernelGGL((prefill_mfma_long_kernel<GQ>), dim3((unsigned)grid), dim3(pfl::kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((prefill_mfma_kernel<GQ>), dim3((unsigned)grid), dim3(pfc::kThreads), 0, stream, a);
+        launch_small<GQ, false, false>(a, grid, stream);
     return hipGetLastError();
 }
 
@@ -941,8 +1030,7 @@ hipError_t run_prefill_planned(const PrefillArgs &a, int layout, int entries, hi
         hipLaunchKernelGGL((prefill_mfma_long_kernel<GQ, true>), dim3((unsigned)grid), dim3(pfl::kThreads), 0, stream,
                            a);
     else
-        hipLaunchKernelGGL((prefill_mfma_kernel<GQ, false, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0,
-                           stream, a);
+        launch_small<GQ, false, true>(a, grid, stream);
     return hipGetLastError();
 }
 
@@ -979,10 +1067,10 @@ hipError_t launch_prefill_shared(const PrefillArgs &a, hipStream_t stream) {
     if (grid < 1) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     switch (g) {
-        case 1: hipLaunchKernelGGL((prefill_mfma_kernel<1, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((prefill_mfma_kernel<2, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((prefill_mfma_kernel<4, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((prefill_mfma_kernel<8, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0, stream, a); break;
+        case 1: launch_small<1, true, false>(a, grid, stream); break;
+        case 2: launch_small<2, true, false>(a, grid, stream); break;
+        case 4: launch_small<4, true, false>(a, grid, stream); break;
+        case 8: launch_small<8, true, false>(a, grid, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
