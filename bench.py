@@ -7,12 +7,18 @@ One step = the whole hot path on synthetic inputs already resident in HBM:
   bf16, batch 256, lognormal context lengths, page_size 1 by default) as one
   replay of the captured HIP graph: store_kv of the 256 new tokens, then
   split-K decode attention (and its merge);
+* the same step at the other page size (16 by default: same lengths and
+  logical K/V, shuffled pages);
+* the decode step of a Qwen3-0.6B-shaped layer (16 q / 8 kv heads, batch 64,
+  contexts U[512, 4096]), captured the same way;
 * a ragged causal prefill/extend step (Qwen3-0.6B heads, 8 requests, extend
   U[128, 2048] on a cached prefix U[0, 1024]): store_kv, then MFMA prefill
   attention.
 
-``value`` is the decode leg's achieved HBM bandwidth (algorithmic bytes / leg
-time); the same line carries req-tokens/s of the decode leg and the prefill
+``value`` is the first decode leg's achieved HBM bandwidth (algorithmic bytes
+/ leg time); the line carries the other decode legs' figures (and the captured
+steps of both page sizes replayed one at a time after a cache flush),
+req-tokens/s of the decode leg and the prefill
 leg's TFLOP/s, a roofline object for the dominant kernel (decode attention,
 timed with HIP events on its own stream) and the fp64 CPU oracle timed on the
 same decode workload as a reported baseline.
@@ -623,9 +629,13 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
-    log("building decode workload (Qwen3-8B shape, bs 256) on the GPU")
+    log("building decode workloads (Qwen3-8B shape, bs 256, page sizes 1 and 16) on the GPU")
     w4 = wl.qwen3_8b_decode(page_size=args.page_size, device=dev)
+    # the same lengths and logical K/V at the other page size (both are the decode gate)
+    w4o = wl.qwen3_8b_decode(page_size=17 - args.page_size, device=dev)
     log(f"  sum(L)={int(w4.seq_lens.sum())} max L={int(w4.seq_lens.max())} ({time.time() - t0:.1f}s)")
+    w2 = wl.qwen3_06b_decode(device=dev)
+    log(f"  qwen3-0.6b decode bs {w2.bs}: sum(L)={int(w2.seq_lens.sum())} ({time.time() - t0:.1f}s)")
     w3 = wl.ragged_prefill(device=dev)
     log(f"  prefill tokens={w3.num_tokens} ctx={int(w3.seq_lens.sum())} ({time.time() - t0:.1f}s)")
     torch.cuda.synchronize()
@@ -642,6 +652,20 @@ def main() -> int:
                                               w4.q, w4.page_table, w4.table_idx, w4.seq_lens,
                                               w4.max_seq_len, ws4, page_size=w4.page_size,
                                               chunk=args.chunk, sm_scale=w4.sm_scale, stream=stream)
+    # the other page size's step, and the Qwen3-0.6B decode batch (bs 64), each
+    # as a captured step of its own (store_kv + decode attention)
+    side = {}
+    for tag, w in ((f"ps{w4o.page_size}", w4o), ("qwen3_06b_bs64", w2)):
+        o = torch.empty_like(w.q)
+        l = torch.empty(w.bs, w.q_heads, dtype=torch.float32, device=dev)
+        ws = _lib.decode_workspace(w.bs, w.q_heads, w.head_dim, w.max_seq_len, args.chunk, device=dev)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g = _lib.msgl_decode_graph_create(w.k_pool, w.v_pool, w.k_new, w.v_new, w.out_loc, o, l, w.q,
+                                              w.page_table, w.table_idx, w.seq_lens, w.max_seq_len, ws,
+                                              page_size=w.page_size, chunk=args.chunk, sm_scale=w.sm_scale,
+                                              stream=stream)
+        side[tag] = (w, g, (o, l, ws))
     out3 = torch.empty_like(w3.q)
     lse3 = torch.empty(w3.num_tokens, w3.q_heads, dtype=torch.float32, device=dev)
     max_ext3 = int((w3.seq_lens - w3.cached_lens).max())
@@ -655,29 +679,33 @@ def main() -> int:
     # settle: the first few tens of steps after matrix work starts run the decode leg 10-15%
     # slower (a start-up transient of the clocks or power state: it is gone after ~50 steps
     # and does not come back); full steps, untimed, before the W warm-up steps
+    # One step: the captured decode step at page size 1, the same at page size
+    # 16, the Qwen3-0.6B decode step, then the prefill leg.
+    g_o, g_2 = side[f"ps{w4o.page_size}"][1], side["qwen3_06b_bs64"][1]
+
+    legs = [lambda: graph.launch(stream), lambda: g_o.launch(stream), lambda: g_2.launch(stream), prefill_leg]
+
     log(f"settle {SETTLE_STEPS} steps, warmup {args.warmup} steps")
     for _ in range(SETTLE_STEPS + args.warmup):
-        graph.launch(stream)
-        prefill_leg()
+        for leg in legs:
+            leg()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    n_legs = len(legs)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_legs + 1)] for _ in range(K)]
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(K):
-        a, b, c = ev[i]
-        a.record(stream)
-        graph.launch(stream)
-        b.record(stream)
-        prefill_leg()
-        c.record(stream)
+        ev[i][0].record(stream)
+        for j, leg in enumerate(legs):
+            leg()
+            ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    dec_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    pre_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    leg_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / K for j in range(n_legs)]
+    dec_ms, dec_o_ms, dec2_ms, pre_ms = leg_ms
     ms_per_step = wall * 1e3 / K
 
     # dominant kernel: decode attention on its own, eager, HIP events on its stream
@@ -793,6 +821,14 @@ def main() -> int:
     dflush = flushed_timing(lambda: runner.decode_attn(w4, k_pool4, v_pool4, out=out4, lse=lse4, workspace=ws4,
                                                        chunk=args.chunk, stream=stream), stream, 30)
     dflush["GBs"] = round(decode_bytes(w4) / (dflush["median_ms"] * 1e-3) / 1e9, 1)
+    # the captured steps at both page sizes, replayed one at a time after the flush
+    gflush = {}
+    for tag, w, g in ((f"ps{w4.page_size}", w4, graph), (f"ps{w4o.page_size}", w4o, g_o)):
+        f = flushed_timing(lambda g=g: g.launch(stream), stream, 30)
+        gbs = (decode_bytes(w) + store_bytes(w)) / (f["median_ms"] * 1e-3) / 1e9
+        f["GBs"] = round(gbs, 1)
+        f["frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+        gflush[tag] = f
     pflush = flushed_timing(prefill_attn_only, stream, 50)
     pflush["TFLOPs"] = round(prefill_flops(w3) / (pflush["median_ms"] * 1e-3) / 1e12, 1)
     pflush["frac_bf16_peak"] = round(pflush["TFLOPs"] / BF16_DENSE_PEAK_TFLOPS, 4)
@@ -805,6 +841,16 @@ def main() -> int:
     prefill_tflops = flops3 / (pre_ms * 1e-3) / 1e12
     pattn_tflops = flops3 / (pattn_ms * 1e-3) / 1e12
     req_tok_s = w4.bs / (dec_ms * 1e-3)
+
+    def graph_leg(w, ms):
+        gbs = (decode_bytes(w) + store_bytes(w)) / (ms * 1e-3) / 1e9
+        return {"batch": w.bs, "q_heads": w.q_heads, "kv_heads": w.kv_heads, "page_size": w.page_size,
+                "context_tokens": int(w.seq_lens.sum()), "ms": round(ms, 4), "GBs": round(gbs, 1),
+                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "req_tokens_per_s": round(w.bs / (ms * 1e-3), 1),
+                "bytes": decode_bytes(w) + store_bytes(w)}
+
+    decode_graph = {f"ps{w4.page_size}": graph_leg(w4, dec_ms), f"ps{w4o.page_size}": graph_leg(w4o, dec_o_ms)}
+    config2 = graph_leg(w2, dec2_ms)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -852,7 +898,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"qwen3-8b decode bs256 ps{w4.page_size} (hipGraph: store_kv + decode attn) "
+            "workload": f"qwen3-8b decode bs256 ps{w4.page_size} (hipGraph: store_kv + decode attn; value) "
+                        f"+ the same at ps{w4o.page_size} + qwen3-0.6b decode bs64 (hipGraph) "
                         f"+ ragged prefill 8 req (store_kv + prefill attn)",
             "decode": {"batch": w4.bs, "q_heads": w4.q_heads, "kv_heads": w4.kv_heads,
                        "head_dim": w4.head_dim, "page_size": w4.page_size,
@@ -863,6 +910,9 @@ def main() -> int:
                         "context_tokens": int(w3.seq_lens.sum())},
         },
         "decode_leg_ms": round(dec_ms, 4),
+        "decode_graph_step": decode_graph,
+        "decode_graph_flushed": gflush,
+        "qwen3_06b_decode_bs64": config2,
         "prefill_leg_ms": round(pre_ms, 4),
         "req_tokens_per_s": round(req_tok_s, 1),
         "prefill_tflops": round(prefill_tflops, 2),
@@ -883,6 +933,8 @@ def main() -> int:
         "cpu_baseline": cpu,
     }
     graph.destroy()
+    for _, g, _ in side.values():
+        g.destroy()
     if args.copy_calibration_gib > 0:
         n = int(args.copy_calibration_gib * (1 << 30)) // 4
         x = torch.ones(n, dtype=torch.float32, device=dev)

@@ -25,10 +25,11 @@ def mods():
     return _lib, runner, workloads
 
 
-def _round_inputs(wl, w, r, real):
+def _round_inputs(wl, w, r, real, rounds):
     """Decode round r of the first `real` requests: every request is r tokens
-    longer than at round 0; its new token sits at position seq_len - 1."""
-    seq = (w.seq_lens[:real] - ROUNDS + r).clone()
+    longer than at round 0 (the last round ends at the workload's lengths); its
+    new token sits at position seq_len - 1."""
+    seq = (w.seq_lens[:real] - rounds + 1 + r).clone()
     rows = w.table_idx[:real]
     loc = w.page_table[rows.long(), (seq - 1).long()].to(torch.int32)
     tok = torch.arange(real, dtype=torch.int64) + 1000 * (r + 1)
@@ -39,13 +40,15 @@ def _round_inputs(wl, w, r, real):
     return seq, loc, k_new, v_new, q
 
 
-@pytest.mark.parametrize("page_size,real,padded", [(1, 3, 4), (16, 3, 4), (16, 100, 128)])
-def test_graph_padded_replay_matches_eager_and_oracle(oracle_mod, mods, page_size, real, padded):
+def _check_padded_replay(oracle_mod, mods, base, page_size, real, padded, rounds):
+    """Record the step at `padded` rows, run `rounds` decode rounds of the
+    first `real` requests through it and through the eager calls; the real
+    rows must be bit-identical to eager and within 2e-2 of the oracle in every
+    round, and every pool slot but the dummy page's bit-exact at the end."""
     _lib, runner, wl = mods
     dev = torch.device("cuda")
-    base = wl.qwen3_8b_decode(page_size=page_size, device=dev, bs=padded, median=700.0, hi=8192,
-                              num_slots=1 << 20)
-    say(f"[graph] ps={page_size} real={real} padded={padded}")
+    say(f"[graph] ps={page_size} real={real} padded={padded} rounds={rounds} "
+        f"ctx={int(base.seq_lens[:real].sum())}")
     # fixed buffers at the padded size, dummy rows prefilled
     pad = wl.pad_decode(wl.subset_decode(base, real), padded)
     buf = {k: getattr(pad, k).clone() for k in ("q", "k_new", "v_new", "out_loc", "table_idx", "seq_lens")}
@@ -64,8 +67,8 @@ def test_graph_padded_replay_matches_eager_and_oracle(oracle_mod, mods, page_siz
     vp_e = base.v_pool.clone()
     kp_h = base.k_pool.cpu()
     vp_h = base.v_pool.cpu()
-    for r in range(ROUNDS):
-        seq, loc, k_new, v_new, q = _round_inputs(wl, base, r, real)
+    for r in range(rounds):
+        seq, loc, k_new, v_new, q = _round_inputs(wl, base, r, real, rounds)
         # copy this round's values into the recorded buffers (real rows only)
         buf["seq_lens"][:real].copy_(seq)
         buf["out_loc"][:real].copy_(loc)
@@ -87,13 +90,52 @@ def test_graph_padded_replay_matches_eager_and_oracle(oracle_mod, mods, page_siz
         assert torch.equal(lse[:real], lse_e[:real])
         # oracle on host copies of the same inputs
         kp_h, vp_h = oracle_mod.store_kv(kp_h, vp_h, k_new, v_new, loc)
-        ref, _ = oracle_mod.attention(q, kp_h, vp_h, base.page_table, base.table_idx[:real], seq,
-                                      torch.arange(real + 1, dtype=torch.int32))
+        ref, ref_lse = oracle_mod.attention(q, kp_h, vp_h, base.page_table, base.table_idx[:real], seq,
+                                            torch.arange(real + 1, dtype=torch.int32))
         err = max_abs(out[:real], ref)
         say(f"[graph] round {r}: max-abs vs oracle {err:.3e}")
         assert err <= 2e-2
+        assert max_abs(lse[:real], ref_lse) < 1e-3
     assert store_mismatch(base, kp, vp, kp_h, vp_h) == 0
     g.destroy()
+
+
+@pytest.mark.parametrize("page_size,real,padded", [(1, 3, 4), (16, 3, 4), (16, 100, 128)])
+def test_graph_padded_replay_matches_eager_and_oracle(oracle_mod, mods, page_size, real, padded):
+    wl = mods[2]
+    base = wl.qwen3_8b_decode(page_size=page_size, device=torch.device("cuda"), bs=padded, median=700.0,
+                              hi=8192, num_slots=1 << 20)
+    _check_padded_replay(oracle_mod, mods, base, page_size, real, padded, ROUNDS)
+
+
+# The Qwen3-8B decode batch at full size (256 requests, lognormal lengths up to
+# 32768, 2^21 slots), built once per page size and shared by the tests below.
+_CONFIG4 = {}
+
+
+def _config4(wl, page_size):
+    if page_size not in _CONFIG4:
+        _CONFIG4.clear()  # one page size resident at a time
+        torch.cuda.empty_cache()
+        _CONFIG4[page_size] = wl.qwen3_8b_decode(page_size=page_size, device=torch.device("cuda"))
+    return _CONFIG4[page_size]
+
+
+@pytest.mark.parametrize("page_size", [1, 16])
+def test_graph_full_batch_config4(oracle_mod, mods, page_size):
+    # the captured step at the recorded size 256 with all 256 lognormal
+    # requests: the shape the throughput figure is taken on
+    base = _config4(mods[2], page_size)
+    _check_padded_replay(oracle_mod, mods, base, page_size, 256, 256, 3)
+
+
+@pytest.mark.parametrize("page_size", [1, 16])
+@pytest.mark.parametrize("real,padded", [(1, 1), (2, 2), (7, 8), (16, 16), (30, 32), (64, 64), (200, 256)])
+def test_graph_recorded_sizes_config4(oracle_mod, mods, page_size, real, padded):
+    # every other recorded batch size on the same lognormal batch (its first
+    # `real` requests), exactly full or padded with dummy rows
+    base = _config4(mods[2], page_size)
+    _check_padded_replay(oracle_mod, mods, base, page_size, real, padded, 2)
 
 
 def test_graph_reads_only_recorded_buffers(mods):
