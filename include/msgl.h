@@ -179,6 +179,35 @@ msgl_status msgl_decode_attn(void *out, float *lse, const void *q, const void *k
                              void *stream);
 
 /*
+ * msgl_decode_attn_noalloc - msgl_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and result (the
+ * same kernels) with no workspace argument.  The workspace is a fixed device
+ * array of MSGL_NOALLOC_SCRATCH_BYTES inside the library, one per device,
+ * set up at the first call on a device (its address is looked up once, with
+ * that device current) and held until the process ends; the call itself
+ * allocates nothing.  A call whose msgl_decode_workspace_bytes exceeds it
+ * returns MSGL_WORKSPACE_TOO_SMALL and enqueues nothing: at head_dim 128 it
+ * serves up to 944 requests with 32 q heads, 5983 with 16, none with 64.  `stream` must belong to the
+ * current device (else MSGL_INVALID_ARG).  Every call on a device shares that
+ * device's array: calls that overlap on one device (on different streams, or
+ * from several threads without ordering) race and give wrong results.  Other
+ * arguments and preconditions as for msgl_decode_attn.
+ * msgl_noalloc_scratch_bytes returns MSGL_NOALLOC_SCRATCH_BYTES.
+ */
+#define MSGL_NOALLOC_SCRATCH_BYTES (80u << 20)
+
+size_t msgl_noalloc_scratch_bytes(void);
+
+msgl_status msgl_decode_attn_noalloc(void *out, float *lse, const void *q, const void *k_pool,
+                                     const void *v_pool, int64_t num_slots, const int32_t *page_table,
+                                     int32_t row_stride, const int32_t *table_idx,
+                                     const int32_t *seq_lens, int32_t batch, int32_t q_heads,
+                                     int32_t kv_heads, int32_t head_dim, int32_t page_size,
+                                     int32_t max_seq_len, int32_t chunk, float sm_scale,
+                                     msgl_dtype dtype, void *stream);
+
+/*
  * Cascade decode over shared radix prefixes.  The requests of a group (batch
  * rows group_start[g] .. group_start[g+1]-1, consecutive) share the first
  * prefix_lens[b] keys of their page-table rows: the same slot ids, as the

@@ -31,8 +31,8 @@ MSGL_BF16 = 1
 EXPORTS = (
     "msgl_last_error", "msgl_version", "msgl_store_kv", "msgl_rope_store_kv", "msgl_vocab_embed",
     "msgl_decode_workspace_bytes",
-    "msgl_decode_attn", "msgl_prefill_attn", "msgl_decode_graph_create", "msgl_graph_launch",
-    "msgl_graph_destroy", "msgl_validate_batch", "msgl_decode_shared_prefix_workspace_bytes",
+    "msgl_decode_attn", "msgl_decode_attn_noalloc", "msgl_noalloc_scratch_bytes", "msgl_prefill_attn",
+    "msgl_decode_graph_create", "msgl_graph_launch", "msgl_graph_destroy", "msgl_validate_batch", "msgl_decode_shared_prefix_workspace_bytes",
     "msgl_decode_attn_shared_prefix", "msgl_validate_shared_prefix", "msgl_prefill_plan_bytes",
     "msgl_prefill_plan", "msgl_prefill_attn_planned",
 )
@@ -65,6 +65,11 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msgl_decode_attn.restype = st
     lib.msgl_decode_attn.argtypes = [P, P, P, P, P, I64, P, I32, P, P, I32, I32, I32, I32, I32, I32,
                                      I32, F, st, P, SZ, P]
+    lib.msgl_decode_attn_noalloc.restype = st
+    lib.msgl_decode_attn_noalloc.argtypes = [P, P, P, P, P, I64, P, I32, P, P, I32, I32, I32, I32, I32, I32,
+                                             I32, F, st, P]
+    lib.msgl_noalloc_scratch_bytes.restype = SZ
+    lib.msgl_noalloc_scratch_bytes.argtypes = []
     lib.msgl_decode_shared_prefix_workspace_bytes.restype = SZ
     lib.msgl_decode_shared_prefix_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.msgl_decode_attn_shared_prefix.restype = st
@@ -192,6 +197,24 @@ def msgl_decode_attn(out, lse, q, k_pool, v_pool, page_table, table_idx, seq_len
                                 _p(_i32(page_table)), page_table.shape[1], _p(_i32(table_idx)),
                                 _p(_i32(seq_lens)), bs, H, G, d, page_size, max_seq_len, chunk,
                                 sm_scale, _dt(q), _p(workspace), workspace.numel(), _stream(stream)))
+
+
+def msgl_noalloc_scratch_bytes() -> int:
+    return int(lib.msgl_noalloc_scratch_bytes())
+
+
+def msgl_decode_attn_noalloc(out, lse, q, k_pool, v_pool, page_table, table_idx, seq_lens, max_seq_len: int,
+                             page_size: int = 1, chunk: int = 0, sm_scale: Optional[float] = None,
+                             stream=None) -> None:
+    """msgl_decode_attn with the library's fixed scratch in place of a workspace."""
+    bs, H, d = q.shape
+    S, G, _ = k_pool.shape
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    _check(lib.msgl_decode_attn_noalloc(_p(out), _p(lse), _p(q), _p(k_pool), _p(v_pool), S,
+                                        _p(_i32(page_table)), page_table.shape[1], _p(_i32(table_idx)),
+                                        _p(_i32(seq_lens)), bs, H, G, d, page_size, max_seq_len, chunk,
+                                        sm_scale, _dt(q), _stream(stream)))
 
 
 def shared_prefix_workspace(batch: int, q_heads: int, head_dim: int, max_seq_len: int, chunk: int = 0,

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -59,18 +60,18 @@ constexpr int32_t kMaxDecodeBatch = 8192;
 
 int32_t effective_chunk(int32_t chunk) { return chunk == 0 ? msgl::kDefaultChunk : chunk; }
 
-msgl_status check_decode(const void *out, const void *q, const void *k_pool, const void *v_pool,
-                         int64_t num_slots, const int32_t *page_table, int32_t row_stride,
-                         const int32_t *table_idx, const int32_t *seq_lens, int32_t batch,
-                         int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t page_size,
-                         int32_t max_seq_len, int32_t chunk, msgl_dtype dtype, const void *workspace,
-                         size_t workspace_bytes) {
+// Checks of a decode call's scalars and pointers, all but the workspace.
+msgl_status check_decode_args(const void *out, const void *q, const void *k_pool, const void *v_pool,
+                              int64_t num_slots, const int32_t *page_table, int32_t row_stride,
+                              const int32_t *table_idx, const int32_t *seq_lens, int32_t batch,
+                              int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t max_seq_len, int32_t chunk, msgl_dtype dtype) {
     msgl_status s = check_common(dtype, head_dim, kv_heads, num_slots);
     if (s != MSGL_OK) return s;
     if ((s = check_group(q_heads, kv_heads)) != MSGL_OK) return s;
     if (batch < 0 || batch > kMaxDecodeBatch)
         return fail(batch < 0 ? MSGL_INVALID_ARG : MSGL_UNSUPPORTED, "batch %d out of range [0, %d]", batch, kMaxDecodeBatch);
-    if (batch > 0 && (!out || !q || !k_pool || !v_pool || !page_table || !table_idx || !seq_lens || !workspace))
+    if (batch > 0 && (!out || !q || !k_pool || !v_pool || !page_table || !table_idx || !seq_lens))
         return fail(MSGL_INVALID_ARG, "NULL pointer argument");
     if (row_stride < 1) return fail(MSGL_INVALID_ARG, "row_stride %d < 1", row_stride);
     if (max_seq_len < 1 || max_seq_len > row_stride)
@@ -81,7 +82,21 @@ msgl_status check_decode(const void *out, const void *q, const void *k_pool, con
         return fail(MSGL_UNSUPPORTED, "batch %d x (max_seq_len %d + 32) work units reach 2^31", batch, max_seq_len);
     const int32_t c = effective_chunk(chunk);
     if (c < 64 || c % 64 != 0) return fail(MSGL_INVALID_ARG, "chunk %d is not a positive multiple of 64", chunk);
-    const size_t need = msgl::decode_workspace_bytes(batch, q_heads, head_dim, max_seq_len, c);
+    return ok();
+}
+
+msgl_status check_decode(const void *out, const void *q, const void *k_pool, const void *v_pool,
+                         int64_t num_slots, const int32_t *page_table, int32_t row_stride,
+                         const int32_t *table_idx, const int32_t *seq_lens, int32_t batch,
+                         int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t page_size,
+                         int32_t max_seq_len, int32_t chunk, msgl_dtype dtype, const void *workspace,
+                         size_t workspace_bytes) {
+    msgl_status s = check_decode_args(out, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx,
+                                      seq_lens, batch, q_heads, kv_heads, head_dim, page_size, max_seq_len,
+                                      chunk, dtype);
+    if (s != MSGL_OK) return s;
+    if (batch > 0 && !workspace) return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    const size_t need = msgl::decode_workspace_bytes(batch, q_heads, head_dim, max_seq_len, effective_chunk(chunk));
     if (workspace_bytes < need)
         return fail(MSGL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
     return ok();
@@ -161,6 +176,49 @@ struct msgl_graph {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
 };
+
+// ---------------------------------------------------------------------------
+// Decode attention without a caller workspace (msgl_decode_attn_noalloc): the
+// workspace lives in a fixed device array, `scratch`, one copy per device,
+// held for the life of the process.  Host code never passes the array's name
+// to a kernel (on the host it only names a stand-in); the device address is
+// resolved once per device with hipGetSymbolAddress and kept.
+
+static __device__ __align__(256) unsigned char scratch[MSGL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];  // device address of `scratch`, per device (null until resolved)
+
+// Address of the calling device's scratch array.  The stream must belong to
+// the current device (the address is per device).
+msgl_status scratch_address(void *stream, void **addr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MSGL_UNSUPPORTED, "device %d beyond the %d served", dev, kMaxDevices);
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+        if (e != hipSuccess) return from_hip(e, "hipStreamGetDevice");
+        if (sdev != dev)
+            return fail(MSGL_INVALID_ARG, "the stream belongs to device %d, the current device is %d", sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return from_hip(e, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr) return fail(MSGL_HIP_ERROR, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return ok();
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -260,6 +318,37 @@ msgl_status msgl_decode_attn(void *out, float *lse, const void *q, const void *k
     msgl::DecodeArgs a = decode_args(out, lse, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx,
                                      seq_lens, batch, q_heads, kv_heads, head_dim, max_seq_len, chunk,
                                      sm_scale, workspace);
+    return from_hip(msgl::launch_decode(a, static_cast<msgl::DType>(dtype), head_dim,
+                                        static_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
+// Decode attention with the fixed scratch in place of a workspace.
+size_t msgl_noalloc_scratch_bytes(void) { return MSGL_NOALLOC_SCRATCH_BYTES; }
+
+msgl_status msgl_decode_attn_noalloc(void *out, float *lse, const void *q, const void *k_pool,
+                                     const void *v_pool, int64_t num_slots, const int32_t *page_table,
+                                     int32_t row_stride, const int32_t *table_idx,
+                                     const int32_t *seq_lens, int32_t batch, int32_t q_heads,
+                                     int32_t kv_heads, int32_t head_dim, int32_t page_size,
+                                     int32_t max_seq_len, int32_t chunk, float sm_scale,
+                                     msgl_dtype dtype, void *stream) {
+    msgl_status s = check_decode_args(out, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx,
+                                      seq_lens, batch, q_heads, kv_heads, head_dim, page_size, max_seq_len,
+                                      chunk, dtype);
+    if (s != MSGL_OK) return s;
+    const size_t need = msgl::decode_workspace_bytes(batch, q_heads, head_dim, max_seq_len, effective_chunk(chunk));
+    if (need > (size_t)MSGL_NOALLOC_SCRATCH_BYTES)
+        return fail(MSGL_WORKSPACE_TOO_SMALL,
+                    "batch %d x %d q heads x head_dim %d needs %zu bytes of workspace, beyond the %zu of the "
+                    "fixed scratch (msgl_decode_attn with a workspace serves it)",
+                    batch, q_heads, head_dim, need, (size_t)MSGL_NOALLOC_SCRATCH_BYTES);
+    if (batch == 0) return ok();
+    void *ws = nullptr;
+    if ((s = scratch_address(stream, &ws)) != MSGL_OK) return s;
+    msgl::DecodeArgs a = decode_args(out, lse, q, k_pool, v_pool, num_slots, page_table, row_stride, table_idx,
+                                     seq_lens, batch, q_heads, kv_heads, head_dim, max_seq_len, chunk,
+                                     sm_scale, ws);
     return from_hip(msgl::launch_decode(a, static_cast<msgl::DType>(dtype), head_dim,
                                         static_cast<hipStream_t>(stream)),
                     "decode launch");
