@@ -650,7 +650,12 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 //    what came before; this branch is rare and, so that none of it runs on
 //    the common path, its inputs go through an opaque copy.
 //  - Each wave stops computing after its last tile (the one holding its last
-//    query's key); it still takes part in every tile's copies and barrier.
+//    query's key), and skips that tile's second half when every key there
+//    lies past its queries; it still takes part in every tile's copies and
+//    barrier.
+//  - The page-table ids of a tile are copied four tiles ahead, and a wave
+//    reads the ids of its next tile's gathers into registers a tile early, so
+//    the gathers issue right after the barrier without waiting on LDS.
 //
 // In shared-prefix mode (SH, decode requests grouped by a shared radix prefix)
 // the block id also carries a key split s < a.splits: the block attends its
@@ -705,9 +710,9 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     const int pos = SH ? pos0 : pos0 + tok;
     // this wave's last tile: the one holding its last valid query's last key (-1: no valid query)
     const int wfirst = (wave * pf::kColsW) / GQ;
-    const int tw = wfirst >= ntok ? -1
-                   : SH       ? ntiles - 1
-                              : (pos0 + min(ntok - 1, (wave * pf::kColsW + pf::kColsW - 1) / GQ)) / pf::kKT;
+    // this wave's last key (the position of its last valid query) and the tile holding it
+    const int wlast = SH ? pos0 : pos0 + min(ntok - 1, (wave * pf::kColsW + pf::kColsW - 1) / GQ);
+    const int tw = wfirst >= ntok ? -1 : wlast / pf::kKT;
 
     if constexpr (SH) {
         if (nkeys <= 0) {  // an empty split: an empty softmax state, marked by lse = -inf
@@ -735,10 +740,13 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         lane_off[i] = (uint32_t)kvh * pf::kRow + (((lane & 15) ^ row_code(pfc::kRowsW * wave + 4 * i + grp)) << 4);
-    // gathers of tile t into ring stage t % 2: this wave's 4 instructions
-    auto gather = [&](int t, bool is_v) __attribute__((always_inline)) {
-        const u32x4_t ids = *(const __attribute__((address_space(3))) u32x4_t *)(uintptr_t)(
+    // this wave's 4 ids of tile t (its rows' slots), read from the tile's id slot
+    auto read_ids = [&](int t) __attribute__((always_inline)) {
+        return *(const __attribute__((address_space(3))) u32x4_t *)(uintptr_t)(
             ids_wave + (t % pf::kIdSlots) * pf::kKT * 4 + (pfc::kRowsW * wave + 4 * grp) * 4);
+    };
+    // gathers of tile t into ring stage t % 2: this wave's 4 instructions
+    auto gather = [&](int t, bool is_v, const u32x4_t ids) __attribute__((always_inline)) {
         const uint32_t base = lds0 + (t & 1) * pf::kTile + (is_v ? pfc::kVBase : pfc::kKBase) + pfc::kRowsW * wave * pf::kRow;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -753,13 +761,18 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
         }
     };
 
-    // prologue: ids of tiles 0..2, K of tiles 0 and 1, V of tile 0, then Q and a full wait
+    // prologue: ids of tiles 0..3, K of tiles 0 and 1, V of tile 0, then Q and a full wait; the
+    // ids of the first tile's gathers (K of 2, V of 1) go to registers
 #pragma unroll
-    for (int t = 0; t < 3; ++t) copy_ids(t);
+    for (int t = 0; t < 4; ++t) copy_ids(t);
     wait_vmcnt<0>();
-    gather(0, false);
-    if (ntiles > 1) gather(1, false);
-    gather(0, true);
+    {
+        const u32x4_t id0 = read_ids(0);
+        gather(0, false, id0);
+        if (ntiles > 1) gather(1, false, read_ids(1));
+        gather(0, true, id0);
+    }
+    u32x4_t kid = read_ids(2), vid = read_ids(1);
     // Q^T operands as in the single-block layout; the empty asm makes the
     // compiler wait for them here, and the explicit wait covers the copies
     bf16x8_t qv[8];
@@ -895,13 +908,17 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     // start of tile t: wait for this wave's copies, barrier; but at the last
     // tile, refill the ring stages tile t-1 used with K of t+2 and V of t+1
     // and copy the ids of t+3
+    // (the ids of tile t+4 go to the slot tile t's ids held, last read a tile earlier; the ids of
+    // the next tile's gathers are read into registers here, a tile before their use)
     auto tile_start = [&](int t) __attribute__((always_inline)) {
         wait_vmcnt<0>();
         lds_barrier();
         if (t < ntiles - 1) {
-            if (t + 3 < ntiles) copy_ids(t + 3);
-            if (t + 2 < ntiles) gather(t + 2, false);
-            gather(t + 1, true);
+            if (t + 4 < ntiles) copy_ids(t + 4);
+            if (t + 2 < ntiles) gather(t + 2, false, kid);
+            gather(t + 1, true, vid);
+            kid = read_ids(t + 3);
+            vid = read_ids(t + 2);
         }
     };
     auto tile = [&](int t, int stage) __attribute__((always_inline)) {
@@ -931,12 +948,14 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     }
     if (tw >= 0) {  // this wave's last tile (V of it was copied in the tile before)
         tile_start(t);
+        // its second half lies past every key of this wave: no softmax and no P.V for it
+        const bool half = (wlast & (pf::kKT - 1)) < pf::kKT / 2;
         if (t & 1) {
-            unit(2 * t, 1, 0, false, true);
-            unit(2 * t + 1, 1, 0, false, false);
+            unit(2 * t, 1, 0, false, !half);
+            if (!half) unit(2 * t + 1, 1, 0, false, false);
         } else {
-            unit(2 * t, 0, 1, false, true);
-            unit(2 * t + 1, 0, 1, false, false);
+            unit(2 * t, 0, 1, false, !half);
+            if (!half) unit(2 * t + 1, 0, 1, false, false);
         }
         ++t;
     }
