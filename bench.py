@@ -526,12 +526,16 @@ def mixed(iters: int) -> int:
 
 def prefill_profile(iters: int) -> int:
     """Only the ragged prefill attention (8 requests, Qwen3-0.6B heads),
-    launched back to back: the command the prefill counter profiles run."""
+    launched back to back: the command the prefill counter profiles run.  The
+    new tokens' K/V are written into the pools first, as in the step: with
+    their slots still zero the kernel runs several percent faster (the matrix
+    cores draw less power on zero operands and the clocks stay higher)."""
     import torch
-    from paged_kv_attention_slots_amd import _lib, workloads as wl
+    from paged_kv_attention_slots_amd import _lib, runner, workloads as wl
 
     dev = torch.device("cuda:0")
     w = wl.ragged_prefill(device=dev)
+    runner.store_kv(w, w.k_pool, w.v_pool)
     out = torch.empty_like(w.q)
     lse = torch.empty(w.num_tokens, w.q_heads, dtype=torch.float32, device=dev)
     me = int((w.seq_lens - w.cached_lens).max())
@@ -576,7 +580,63 @@ def ceilings(iters: int) -> int:
     gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
     print(json.dumps({"ceiling": "device copy (torch copy_, 2 GiB read + 2 GiB written)", "ms": round(ms, 4),
                       "GBs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+    del x, y
+    read_ceilings(iters, stream)
     return 0
+
+
+def read_ceilings(iters: int, stream) -> None:
+    """Read ceilings of the decode kernel's access patterns, from the probe
+    kernels in csrc/probes (libmsgl_probes.so): a sequential stream of 16-byte
+    loads over 4 GiB, and a 4 GiB pool of 2 KB rows (8 kv heads x 128 bf16)
+    read as 256-byte per-head slices of rows in random order (page size 1) and
+    of random 16-row pages (page size 16).  Each is the best over a few grid
+    sizes; one JSON line each."""
+    import ctypes
+
+    import torch
+
+    from paged_kv_attention_slots_amd import build as _build
+
+    lib = ctypes.CDLL(_build.PROBES_PATH)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.msglp_stream_read.argtypes = [P, I64, P, I, P]
+    lib.msglp_gather_heads.argtypes = [P, P, I, I, I, P, I, P]
+    dev = stream.device
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    heads, row_bytes = 8, 8 * 256
+    rows = nbytes // row_bytes
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    row_ids = torch.randperm(rows, generator=gen, device=dev).to(torch.int32)
+    page_ids = torch.randperm(rows // 16, generator=gen, device=dev).to(torch.int32)
+    assert int(row_ids.max()) < rows and int(page_ids.max()) < rows // 16
+    s = stream.cuda_stream
+
+    def best(call, grids):
+        out = []
+        for g in grids:
+            assert call(g) == 0
+            out.append((_time_stream(lambda: call(g), stream, iters, warm=3), g))
+        return min(out)
+
+    for name, call, grids in (
+            ("sequential read, 16-byte nontemporal loads, 4 GiB",
+             lambda g: lib.msglp_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), g, s), (cus, 2 * cus, 4 * cus)),
+            ("random 2 KB rows read as 256-byte head slices (page size 1), 4 GiB pool",
+             lambda g: lib.msglp_gather_heads(buf.data_ptr(), row_ids.data_ptr(), rows, heads, 0, sink.data_ptr(), g, s),
+             (cus // 4, cus // 2, cus, 2 * cus)),
+            ("random 16-row pages read as 256-byte head slices (page size 16), 4 GiB pool",
+             lambda g: lib.msglp_gather_heads(buf.data_ptr(), page_ids.data_ptr(), rows // 16, heads, 1,
+                                              sink.data_ptr(), g, s),
+             (cus // 4, cus // 2, cus, 2 * cus))):
+        ms, g = best(call, grids)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        print(json.dumps({"ceiling": name, "ms": round(ms, 4), "GBs": round(gbs, 1),
+                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "blocks": g}), flush=True)
 
 
 def main() -> int:

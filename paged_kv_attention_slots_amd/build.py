@@ -2,7 +2,9 @@
 
 Every HIP translation unit is compiled with hipcc for gfx950 only, with the
 packed-fp32 instructions disabled, then linked into one shared library next to
-this file.  ``python -m paged_kv_attention_slots_amd.build`` rebuilds it.
+this file.  The bench's read-ceiling probes (csrc/probes) go into a library of
+their own, libmsgl_probes.so.  ``python -m paged_kv_attention_slots_amd.build``
+rebuilds both.
 """
 
 from __future__ import annotations
@@ -17,6 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB_PATH = os.path.join(HERE, "libmsgl.so")
+# read-bandwidth probes for the bench's ceilings (measurement only, not part of libmsgl)
+PROBES_PATH = os.path.join(HERE, "libmsgl_probes.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -64,6 +68,13 @@ def build(jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB_PATH)
+    probes = sorted(glob.glob(os.path.join(CSRC, "probes", "*.hip")))
+    tmp = PROBES_PATH + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *COMMON_FLAGS, "-shared", "-o", tmp, *probes]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBES_PATH)
     return LIB_PATH
 
 
