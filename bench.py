@@ -36,6 +36,9 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+# template arguments of the Qwen3-8B-shaped decode kernels in profiler kernel names
+# (element type, head_dim 128, 4 q heads per kv head)
+QWEN3_8B_DECODE = ", 128, 4"
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -142,8 +145,9 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes,
     os.makedirs(PROFILE_DIR, exist_ok=True)
     lines = ["# rocprofv3 --kernel-trace --stats summary of the benchmark command",
              f"# command: rocprofv3 --kernel-trace --stats --output-format csv -- {command}",
-             "# workload: Qwen3-8B decode bs 256 page_size 1 (graph + eager decode-attention launches),",
-             "#           ragged prefill 8 requests (Qwen3-0.6B heads), then the fused RoPE, vocabulary",
+             "# workload: Qwen3-8B decode bs 256 as captured steps at page sizes 1 and 16, the Qwen3-0.6B",
+             "#           decode bs 64 captured step, ragged prefill 8 requests (Qwen3-0.6B heads), eager",
+             "#           decode-attention launches (bs 256, page size 1), then the fused RoPE, vocabulary",
              "#           indexing and shared-prefix legs; durations in microseconds", ""]
     head = f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_%':>8}  kernel"
     mine = [r for r in stats if "msgl::" in r["Name"]]
@@ -169,13 +173,14 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes,
             out.append(f"{len(d):6d} {sum(d) / len(d):10.2f} {min(d):10.2f} {max(d):10.2f} {'':>8}  {name[:110]}")
         return out
     lines += ["## library kernels, whole run", head] + [row(r) for r in mine]
-    lines += ["", "## the decode step (Qwen3-8B bs 256: graph replays, then eager launches) and the ragged prefill",
+    lines += ["", "## the step's legs (decode graph replays at bs 256 ps1 and ps16 and at bs 64, the ragged prefill),",
+              "## then the eager launches the bench times alone (decode attention, prefill attention)",
               head] + legs(True)
     # the roofline's kernel: the eager decode-attention launches the bench line times (the
     # last KERNEL_ITERS split + merge pairs before the cut) against its HIP-event average
     def eager(kind):
         d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
-             if kind in r["Kernel_Name"] and int(r["Dispatch_Id"]) < cut]
+             if kind in r["Kernel_Name"] and QWEN3_8B_DECODE in r["Kernel_Name"] and int(r["Dispatch_Id"]) < cut]
         return d[-KERNEL_ITERS:]
     sp, mg = eager("decode_split_kernel"), eager("decode_merge_kernel")
     if sp and mg:
@@ -205,31 +210,42 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, command, workload_bytes,
     fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
     write = per_dispatch(write_dir, "WRITE_SIZE")
 
-    def one(d, key):
-        names = [n for n in d if key in n]
+    def one(d, key, shape=""):
+        names = [n for n in d if key in n and shape in n]
         if not names:
             raise KeyError(key)
         vals = d[names[0]]
         return sum(vals) / len(vals), len(vals)
 
-    neg_f, _ = one(fetch, "neg_kernel")
-    neg_w, _ = one(write, "neg_kernel")
+    def copies(d):
+        # the calibration copies: 3 of 1 GiB, then 3 of a quarter of that (see --copy-calibration-gib)
+        names = [n for n in d if "neg_kernel" in n]
+        vals = sorted(v for n in names for v in d[n])
+        if len(vals) < 6:
+            raise KeyError("calibration copies")
+        return sum(vals[-3:]) / 3, sum(vals[:3]) / 3
+
     cal = float(1 << 30)  # the bench negates 1 GiB (--copy-calibration-gib 1): 1 GiB read, 1 GiB written
+    (neg_f, neg_f4), (neg_w, neg_w4) = copies(fetch), copies(write)
     f_scale, w_scale = cal / neg_f, cal / neg_w
-    split_f, n_split = one(fetch, "decode_split_kernel")
-    split_w, _ = one(write, "decode_split_kernel")
-    merge_f, _ = one(fetch, "decode_merge_kernel")
-    merge_w, _ = one(write, "decode_merge_kernel")
+    f_scale4, w_scale4 = cal / 4 / neg_f4, cal / 4 / neg_w4
+    split_f, n_split = one(fetch, "decode_split_kernel", QWEN3_8B_DECODE)
+    split_w, _ = one(write, "decode_split_kernel", QWEN3_8B_DECODE)
+    merge_f, _ = one(fetch, "decode_merge_kernel", QWEN3_8B_DECODE)
+    merge_w, _ = one(write, "decode_merge_kernel", QWEN3_8B_DECODE)
     traffic = (split_f + merge_f) * f_scale + (split_w + merge_w) * w_scale
     lines = [
         "# HBM traffic of one decode-attention launch (split + merge kernels), Qwen3-8B shape, bs 256",
         f"# command (three runs): rocprofv3 --kernel-trace --stats | --pmc FETCH_SIZE | --pmc WRITE_SIZE "
         f"-- {command}",
-        "# counters are per dispatch (KiB), averaged over the launches on this batch (the graph replays",
-        "# and the eager launches, all before the bench's fused-RoPE leg); each is scaled by",
-        "# (known bytes / counter reading) of a plain copy kernel: torch.neg over 1 GiB of fp32",
+        "# counters are per dispatch (KiB), averaged over the launches of the Qwen3-8B kernels (graph",
+        "# replays at page sizes 1 and 16 and the eager launches, all before the bench's fused-RoPE leg);",
+        "# each is scaled by (known bytes / counter reading) of a plain copy kernel: torch.neg over 1 GiB",
+        "# of fp32; the same copy over a quarter of that gives the second pair of factors (a check)",
         f"copy_fetch_scale = {f_scale:.4f}",
         f"copy_write_scale = {w_scale:.4f}",
+        f"copy_fetch_scale_quarter_size = {f_scale4:.4f}",
+        f"copy_write_scale_quarter_size = {w_scale4:.4f}",
         f"split_fetch_bytes = {split_f:.0f}",
         f"split_write_bytes = {split_w:.0f}",
         f"merge_fetch_bytes = {merge_f:.0f}",
@@ -434,6 +450,16 @@ def sweep(iters: int) -> int:
                                    stream=stream)
             torch.cuda.synchronize()
             del wout, wws
+            # the first graph a process creates and replays runs slow for a while: one untimed graph first
+            w = wl.pad_decode(wl.subset_decode(full, 1), 1)
+            out = torch.empty_like(w.q)
+            ws = _lib.decode_workspace(1, w.q_heads, w.head_dim, w.max_seq_len, device=dev)
+            torch.cuda.synchronize()
+            g = _lib.msgl_decode_graph_create(w.k_pool, w.v_pool, w.k_new, w.v_new, w.out_loc, out, None, w.q,
+                                              w.page_table, w.table_idx, w.seq_lens, w.max_seq_len, ws,
+                                              page_size=ps, stream=stream)
+            _time_stream(lambda: g.launch(stream), stream, 200)
+            g.destroy()
         runs = [(n, n) for n in wl.GRAPH_BATCH_SIZES] + [(3, 4), (100, 128), (200, 256)]
         for real, padded in runs:
             w = wl.pad_decode(wl.subset_decode(full, real), padded)
@@ -468,6 +494,7 @@ def sweep(iters: int) -> int:
                  device=dev, n_req=2, e_lo=2048, e_hi=2048, c_lo=8192, c_hi=8192, num_slots=1 << 15,
                  heads=wl.QWEN3_8B, seed=1005))]
     for name, w in cases:
+        runner.store_kv(w, w.k_pool, w.v_pool)  # the new tokens' K/V in the pools, as in the step
         out = torch.empty_like(w.q)
         ms = _time_stream(lambda: runner.prefill_attn(w, w.k_pool, w.v_pool, out=out, with_lse=False,
                                                       stream=stream), stream, iters, warm=PREFILL_WARM_LAUNCHES)
@@ -524,7 +551,7 @@ def mixed(iters: int) -> int:
     return 0
 
 
-def prefill_profile(iters: int) -> int:
+def prefill_profile(iters: int, zero_new: bool = False) -> int:
     """Only the ragged prefill attention (8 requests, Qwen3-0.6B heads),
     launched back to back: the command the prefill counter profiles run.  The
     new tokens' K/V are written into the pools first, as in the step: with
@@ -535,7 +562,8 @@ def prefill_profile(iters: int) -> int:
 
     dev = torch.device("cuda:0")
     w = wl.ragged_prefill(device=dev)
-    runner.store_kv(w, w.k_pool, w.v_pool)
+    if not zero_new:  # --zero-new: leave the new tokens' slots zero (to show the effect above)
+        runner.store_kv(w, w.k_pool, w.v_pool)
     out = torch.empty_like(w.q)
     lse = torch.empty(w.num_tokens, w.q_heads, dtype=torch.float32, device=dev)
     me = int((w.seq_lens - w.cached_lens).max())
@@ -547,7 +575,8 @@ def prefill_profile(iters: int) -> int:
                                stream=stream)
 
     ms = _time_stream(call, stream, iters, warm=PREFILL_WARM_LAUNCHES)
-    print(json.dumps({"prefill_profile": "ragged prefill 8 req", "launches": iters + PREFILL_WARM_LAUNCHES,
+    print(json.dumps({"prefill_profile": "ragged prefill 8 req", "new_token_slots": "zero" if zero_new else "stored",
+                      "launches": iters + PREFILL_WARM_LAUNCHES,
                       "timed_launches": iters, "ms": round(ms, 4),
                       "tflops": round(prefill_flops(w) / (ms * 1e-3) / 1e12, 2)}), flush=True)
     return 0
@@ -641,7 +670,7 @@ def read_ceilings(iters: int, stream) -> None:
 
 def main() -> int:
     if len(sys.argv) > 1 and sys.argv[1] == "--prefill-profile":
-        return prefill_profile(int(sys.argv[2]) if len(sys.argv) > 2 else 20)
+        return prefill_profile(int(sys.argv[2]) if len(sys.argv) > 2 else 20, "--zero-new" in sys.argv)
     if len(sys.argv) > 1 and sys.argv[1] == "--mixed":
         return mixed(int(sys.argv[2]) if len(sys.argv) > 2 else 5)
     if len(sys.argv) > 1 and sys.argv[1] == "--ceilings":
@@ -1001,8 +1030,11 @@ def main() -> int:
         y = torch.empty_like(x)
         for _ in range(3):
             torch.neg(x, out=y)
+        xq, yq = x[:n // 4], y[:n // 4]
+        for _ in range(3):
+            torch.neg(xq, out=yq)
         torch.cuda.synchronize()
-        rec["copy_calibration_bytes"] = n * 4
+        rec["copy_calibration_bytes"] = [n * 4, n // 4 * 4]
     print(json.dumps(rec), flush=True)
     return 0
 
