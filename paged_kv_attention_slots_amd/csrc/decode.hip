@@ -31,6 +31,8 @@ namespace msgl {
 
 // Work units a request costs beyond its keys (see above).
 constexpr int kPieceUnits = 32;
+// Batches up to this size merge with four waves per (request, q head).
+constexpr int kMergeSplitBatch = 64;
 
 // Workspace layout (offsets in bytes):
 //   [0, 256)            control: int64 total work units, int64 share per block
@@ -200,21 +202,28 @@ MSGL_DEV float wave_sum64(float x) {
 }
 
 // Combine the pieces of every request that straddles block boundaries.
-// One wave per (request, q head).  The pieces' (max, sum) states are read
-// lanes-over-pieces, 64 at a time, so a long request costs a few round trips
-// rather than one per piece.  For the outputs the wave splits into four
-// groups of 16 lanes; each lane owns D / 16 consecutive elements, group g
-// takes pieces g, g + 4, ..., and the groups' sums are added by lane exchange
-// at the end, so four pieces' loads are in flight per group.
-template <typename T, int D, int GQ>
+// The pieces' (max, sum) states are read lanes-over-pieces, 64 at a time, so a
+// long request costs a few round trips rather than one per piece.  For the
+// outputs a wave splits into four groups of 16 lanes; each lane owns D / 16
+// consecutive elements.  PW waves share one (request, q head): wave w's group
+// g takes the pieces k with k % (4 PW) == 4 w + g, so that 4 PW pieces' loads
+// are in flight; with PW > 1 the waves' sums meet in LDS.  PW = 1 (a block
+// serves 4 q heads of a request) suits large batches, whose requests are cut
+// into few pieces; PW = 4 suits small ones, where one long request can span
+// tens of pieces and sets the kernel's time.
+template <typename T, int D, int GQ, int PW>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     constexpr int DPL = D / 16;  // elements per lane (a multiple of 4)
+    constexpr int S = 4 * PW;    // piece stride of a group
+    __shared__ float s_acc[PW > 1 ? PW - 1 : 1][D];
     const int b = blockIdx.x;
-    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6;
+    const int h = PW > 1 ? (int)blockIdx.y : blockIdx.y * 4 + wave;
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 4;
+    const int slot = (PW > 1 ? 4 * wave : 0) + grp;
     const int col = (lane & 15) * DPL;
-    if (h >= a.q_heads) return;
+    if (h >= a.q_heads) return;  // uniform over the block when PW > 1
     const int64_t total = a.ctrl[0];
     const int64_t share = a.ctrl[1];
     const int W = a.prefix[b + 1] - a.prefix[b];
@@ -259,8 +268,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         const int cn = min(64, n - c0);
         const float *po = a.part_o + i0 * D + (int64_t)c0 * pstride + col;
 #pragma unroll 4
-        for (int t0 = 0; t0 < cn; t0 += 4) {
-            const int t = t0 + grp;
+        for (int t0 = 0; t0 < cn; t0 += S) {
+            const int t = t0 + slot;
             const float w = __shfl(wk, t & 63);  // every lane takes part; past the end w is unused
             if (t < cn) {
                 const float *pp = po + (int64_t)t * pstride;
@@ -281,6 +290,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         acc[e] += __shfl_xor(acc[e], 32);
     }
     l = wave_sum64(l);
+    if constexpr (PW > 1) {  // waves 1.. hand their sums to wave 0
+        if (wave > 0 && grp == 0)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) s_acc[wave - 1][col + e] = acc[e];
+        __syncthreads();
+        if (wave > 0) return;
+#pragma unroll
+        for (int v = 0; v < PW - 1; ++v)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[e] += s_acc[v][col + e];
+    }
     if (grp != 0) return;
     const float inv = 1.0f / l;
     const int64_t oi = ((int64_t)b * a.q_heads + h) * D + col;
@@ -383,8 +403,11 @@ hipError_t run_decode(const DecodeArgs &a_in, hipStream_t stream, bool prepare_o
                        dim3(threads), smem, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<T, D, GQ>), dim3(a.batch, (a.q_heads + 3) / 4), dim3(256), 0, stream,
-                       a);
+    if (a.batch <= kMergeSplitBatch)
+        hipLaunchKernelGGL((decode_merge_kernel<T, D, GQ, 4>), dim3(a.batch, a.q_heads), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_merge_kernel<T, D, GQ, 1>), dim3(a.batch, (a.q_heads + 3) / 4), dim3(256), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
