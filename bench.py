@@ -833,6 +833,21 @@ def main() -> int:
     torch.cuda.synchronize()
     pattn_ms = ka.elapsed_time(kb) / args.kernel_iters
 
+    # the same launch without the lse output (an engine's prefill asks for none): the kernels then
+    # skip the unrounded weight sums; bit-identical outputs
+    out3n = torch.empty_like(out3)
+
+    def prefill_attn_no_lse():
+        _lib.msgl_prefill_attn(out3n, None, w3.q, w3.k_pool, w3.v_pool, w3.page_table, w3.table_idx,
+                               w3.seq_lens, w3.cached_lens, w3.cu_q, max_ext3, page_size=w3.page_size,
+                               sm_scale=w3.sm_scale, stream=stream)
+
+    nolse_ms = _time_stream(prefill_attn_no_lse, stream, max(100, args.kernel_iters), warm=100)
+    torch.cuda.synchronize()
+    nolse = {"ms": round(nolse_ms, 4), "tflops": round(prefill_flops(w3) / (nolse_ms * 1e-3) / 1e12, 1),
+             "frac_bf16_peak": round(prefill_flops(w3) / (nolse_ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4),
+             "bit_identical": bool(torch.equal(out3n.view(torch.int16), out3.view(torch.int16)))}
+
     # the same launch with the host plan (block list made on the host, copied
     # once): bit-identical outputs, timed in interleaved rounds with the
     # unplanned launch
@@ -1009,6 +1024,7 @@ def main() -> int:
         "prefill_attn_ms": round(pattn_ms, 4),
         "prefill_attn_tflops": round(pattn_tflops, 2),
         "prefill_attn_frac_of_bf16_peak": round(pattn_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+        "prefill_attn_no_lse": nolse,
         "prefill_attn_planned": planned,
         "decode_attn_flushed": dflush,
         "prefill_attn_flushed": pflush,

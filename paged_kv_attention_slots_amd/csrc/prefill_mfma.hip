@@ -50,8 +50,9 @@
 // those rounded weights (a v_dot2 with a pair of ones per pair): the applied
 // weights then sum to one up to float32 rounding (V = 1 gives exactly 1),
 // whatever the size of the weights.  The returned lse comes from a second
-// fp32 sum, of the unrounded weights.  Both sums are lane-partial and are
-// reduced once at the end.
+// fp32 sum, of the unrounded weights, kept only when an lse is asked for (the
+// instances without it save 16 adds per 32 keys).  Both sums are lane-partial
+// and are reduced once at the end.
 //
 // Block ids enumerate the query blocks of all requests densely, in decreasing
 // order of the keys they see (computed in the kernel from the lengths), so the
@@ -352,7 +353,7 @@ MSGL_DEV BlockItem planned_block(const PrefillArgs &a, int i) {
     return {e[0], e[1], e[2], e[3], e[4], e[5]};
 }
 
-template <int GQ, bool PL = false>
+template <int GQ, bool PL, bool LSE>
 __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(PrefillArgs a) {
     constexpr int BQ = pfl::kCols / GQ;  // query tokens per block
     constexpr int S = pfl::kStages;
@@ -512,7 +513,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
             const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, -mu));
             const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, -mu));
             pw[e >> 1] = pack_bf16x2(p0, p1);
-            sum += p0 + p1;
+            if constexpr (LSE) sum += p0 + p1;  // the unrounded sum serves only the lse
             rsum = dot2_bf16(pw[e >> 1], kBf16OnesPair, rsum);
         }
         out[0] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
@@ -612,7 +613,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 
     // normalised by the sum of the weights P.V applied (V = 1 gives 1 exactly);
     // lse from the sum of the unrounded weights
-    lt = add_with_other_half(lt);
+    if constexpr (LSE) lt = add_with_other_half(lt);
     lr = add_with_other_half(lr);
     if (valid) {
         const float inv = 1.0f / lr;
@@ -626,7 +627,8 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
                     make_uint2(pack_bf16x2(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv),
                                pack_bf16x2(acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv));
             }
-        if (a.lse != nullptr && jj == 0) a.lse[(int64_t)(row0 + tl) * a.q_heads + hq] = (m + __log2f(lt)) * kLn2;
+        if constexpr (LSE)
+            if (a.lse != nullptr && jj == 0) a.lse[(int64_t)(row0 + tl) * a.q_heads + hq] = (m + __log2f(lt)) * kLn2;
     }
 }
 
@@ -662,7 +664,7 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 // group's queries to split s of the shared prefix (no causal mask: every
 // query sits after the prefix) and writes the normalised partial output and
 // its lse, in float32, to split s of the partial arrays.
-template <int GQ, bool SH, bool PL, bool O32>
+template <int GQ, bool SH, bool PL, bool O32, bool LSE>
 __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
     constexpr int BQ = pfc::kCols / GQ;  // query tokens per block
     __shared__ __attribute__((aligned(1024))) char smem[pfc::kLds];
@@ -821,11 +823,9 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
     // unit's key 16(e/8) + 4(e%4) + 2((e/4)%2) + jj (see the gathers)
     auto mask = [&](floatx16_t &s, int u) __attribute__((always_inline)) {
         if (32 * u + 31 > pos0) {
+            const int thr = pos - 32 * u - jj;  // element e is masked when its key offset exceeds this
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int key = 32 * u + 16 * (e >> 3) + 4 * (e & 3) + 2 * ((e >> 2) & 1) + jj;
-                s[e] = key > pos ? -INFINITY : s[e];
-            }
+            for (int e = 0; e < 16; ++e) s[e] = 16 * (e >> 3) + 4 * (e & 3) + 2 * ((e >> 2) & 1) > thr ? -INFINITY : s[e];
         }
     };
     auto column_max = [&](const floatx16_t &s) __attribute__((always_inline)) {
@@ -845,7 +845,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
             const float p0 = fast_exp2(fmaf(s[e], a.scale_log2, -mu));
             const float p1 = fast_exp2(fmaf(s[e + 1], a.scale_log2, -mu));
             pw[e >> 1] = pack_bf16x2(p0, p1);
-            sum += p0 + p1;
+            if constexpr (LSE) sum += p0 + p1;  // the unrounded sum serves only the lse
             rsum = dot2_bf16(pw[e >> 1], kBf16OnesPair, rsum);
         }
         out[0] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
@@ -883,7 +883,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
             asm volatile("" ::"v"(pb_new[0]), "v"(pb_new[1]), "v"(lt_u), "v"(lr_u));
         }
         if (has_scores && has_softmax) interleave_unit<1, 4, 2, 8>();
-        if (has_softmax && __any(!(lt_u <= kPrefillWeightBound))) {  // rare
+        if (has_softmax && __any(!(lr_u <= kPrefillWeightBound))) {  // rare
             floatx16_t sr = sc;
             asm volatile("" : "+v"(sr));
             const float mn = fmaxf(m, column_max(sr));
@@ -963,7 +963,7 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
 
     // normalised by the sum of the weights P.V applied (V = 1 gives 1 exactly);
     // lse from the sum of the unrounded weights
-    lt = add_with_other_half(lt);
+    if constexpr (LSE) lt = add_with_other_half(lt);
     lr = add_with_other_half(lr);
     if constexpr (SH) {
         if (valid) {
@@ -993,7 +993,8 @@ __global__ __launch_bounds__(pfc::kThreads, 2) void prefill_mfma_kernel(PrefillA
                     make_uint2(pack_bf16x2(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv),
                                pack_bf16x2(acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv));
             }
-        if (a.lse != nullptr && jj == 0) a.lse[(int64_t)(row0 + tl) * a.q_heads + hq] = (m + __log2f(lt)) * kLn2;
+        if constexpr (LSE)
+            if (a.lse != nullptr && jj == 0) a.lse[(int64_t)(row0 + tl) * a.q_heads + hq] = (m + __log2f(lt)) * kLn2;
     }
 }
 
@@ -1015,15 +1016,31 @@ bool prefill_o32(const PrefillArgs &a) {
     return a.num_slots <= ((int64_t)1 << 24) && (uint64_t)a.num_slots * row_bytes <= ((uint64_t)1 << 32);
 }
 
-// The two-blocks-per-CU kernel with the gather addressing the pool allows.
-template <int GQ, bool SH, bool PL>
-void launch_small(const PrefillArgs &a, int64_t grid, hipStream_t stream) {
-    if (prefill_o32(a))
-        hipLaunchKernelGGL((prefill_mfma_kernel<GQ, SH, PL, true>), dim3((unsigned)grid), dim3(pfc::kThreads), 0,
+// The single-block layout, with the unrounded weight sums only when an lse is asked for.
+template <int GQ, bool PL>
+void launch_long(const PrefillArgs &a, int64_t grid, hipStream_t stream) {
+    if (a.lse != nullptr)
+        hipLaunchKernelGGL((prefill_mfma_long_kernel<GQ, PL, true>), dim3((unsigned)grid), dim3(pfl::kThreads), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((prefill_mfma_kernel<GQ, SH, PL, false>), dim3((unsigned)grid), dim3(pfc::kThreads), 0,
+        hipLaunchKernelGGL((prefill_mfma_long_kernel<GQ, PL, false>), dim3((unsigned)grid), dim3(pfl::kThreads), 0,
                            stream, a);
+}
+
+// The two-blocks-per-CU kernel with the gather addressing the pool allows, and
+// the unrounded weight sums only when an lse is asked for (the shared-prefix
+// mode always writes one).
+template <int GQ, bool SH, bool PL>
+void launch_small(const PrefillArgs &a, int64_t grid, hipStream_t stream) {
+    const dim3 g((unsigned)grid), t(pfc::kThreads);
+    const bool o32 = prefill_o32(a);
+    if (SH || a.lse != nullptr) {
+        if (o32) hipLaunchKernelGGL((prefill_mfma_kernel<GQ, SH, PL, true, true>), g, t, 0, stream, a);
+        else hipLaunchKernelGGL((prefill_mfma_kernel<GQ, SH, PL, false, true>), g, t, 0, stream, a);
+    } else if constexpr (!SH) {
+        if (o32) hipLaunchKernelGGL((prefill_mfma_kernel<GQ, SH, PL, true, false>), g, t, 0, stream, a);
+        else hipLaunchKernelGGL((prefill_mfma_kernel<GQ, SH, PL, false, false>), g, t, 0, stream, a);
+    }
 }
 
 template <int GQ>
@@ -1034,7 +1051,7 @@ hipError_t run_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     if (grid < 1) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (long_chunks)
-        hipLaunchKernelGGL((prefill_mfma_long_kernel<GQ>), dim3((unsigned)grid), dim3(pfl::kThreads), 0, stream, a);
+        launch_long<GQ, false>(a, grid, stream);
     else
         launch_small<GQ, false, false>(a, grid, stream);
     return hipGetLastError();
@@ -1046,8 +1063,7 @@ hipError_t run_prefill_planned(const PrefillArgs &a, int layout, int entries, hi
     if (grid < 1) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (layout == 1)
-        hipLaunchKernelGGL((prefill_mfma_long_kernel<GQ, true>), dim3((unsigned)grid), dim3(pfl::kThreads), 0, stream,
-                           a);
+        launch_long<GQ, true>(a, grid, stream);
     else
         launch_small<GQ, false, true>(a, grid, stream);
     return hipGetLastError();

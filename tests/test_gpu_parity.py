@@ -210,6 +210,21 @@ def test_ragged_prefill_v_ones_exact_sharp(runner, wl, e_lo, e_hi):
     assert bad == 0
 
 
+@pytest.mark.parametrize("heads,e_lo,e_hi", [(None, 1, 300), ("8b", 30, 700), (None, 2048, 2100)])
+def test_prefill_without_lse_is_bit_identical(runner, wl, heads, e_lo, e_hi):
+    # the kernels skip the unrounded weight sums when no lse is asked for; the
+    # output (normalised by the rounded sums either way) must not change
+    w = wl.ragged_prefill(device="cuda", n_req=3, e_lo=e_lo, e_hi=e_hi, c_lo=0, c_hi=400, num_slots=1 << 13,
+                          seed=70 + e_lo, heads=wl.QWEN3_8B if heads == "8b" else wl.QWEN3_06B)
+    kp, vp = w.k_pool.clone(), w.v_pool.clone()
+    runner.store_kv(w, kp, vp)
+    out_l, lse = runner.prefill_attn(w, kp, vp)
+    out_n, none = runner.prefill_attn(w, kp, vp, with_lse=False)
+    torch.cuda.synchronize()
+    assert none is None and torch.isfinite(lse).all()
+    assert torch.equal(out_n.view(torch.int16), out_l.view(torch.int16))
+
+
 def test_length_one_returns_v_bitexact(runner, wl):
     w = wl.qwen3_8b_decode(page_size=1, device="cuda", bs=32, median=1.0, hi=1)
     assert int(w.seq_lens.max()) == 1
