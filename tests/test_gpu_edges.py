@@ -100,3 +100,29 @@ def test_decode_many_one_key_requests(oracle_mod, mods, chunk):
         slot = int(w.page_table[int(w.table_idx[b]), 0])
         v = vp[slot].repeat_interleave(w.q_heads // w.kv_heads, dim=0)
         assert torch.equal(res.out[b].cpu().view(torch.int16), v.view(torch.int16)), b
+
+
+@pytest.mark.parametrize("n_req,e_lo,e_hi", [(3, 1, 300), (2, 2048, 2100)])
+def test_prefill_pool_beyond_4gib(mods, n_req, e_lo, e_hi):
+    # a pool above 4 GiB (2^21 + 64 slots of 2 KB) runs the gathers' 64-bit
+    # addressing; its first rows hold a small workload's pool, so the result
+    # must equal, bit for bit, the same workload on the small pool (32-bit
+    # offsets from the pool base), on both matrix-core layouts
+    runner, wl = mods
+    w = wl.ragged_prefill(device="cuda", n_req=n_req, e_lo=e_lo, e_hi=e_hi, c_lo=0, c_hi=300,
+                          num_slots=1 << 13, seed=80 + e_lo)
+    kp, vp = w.k_pool.clone(), w.v_pool.clone()
+    runner.store_kv(w, kp, vp)
+    big = (1 << 21) + 64
+    kb = torch.zeros(big, w.kv_heads, w.head_dim, dtype=w.dtype, device="cuda")
+    vb = torch.zeros_like(kb)
+    kb[:kp.shape[0]] = kp
+    vb[:vp.shape[0]] = vp
+    assert kb.numel() * kb.element_size() > (1 << 32)
+    say(f"[edge] prefill on a {kb.numel() * kb.element_size() / 2**30:.2f} GiB pool, T={w.num_tokens}")
+    out_s, lse_s = runner.prefill_attn(w, kp, vp)
+    out_b, lse_b = runner.prefill_attn(w, kb, vb)
+    torch.cuda.synchronize()
+    assert torch.equal(out_b.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(lse_b, lse_s)
+    del kb, vb
