@@ -636,9 +636,10 @@ __global__ __launch_bounds__(pfl::kThreads, 2) void prefill_mfma_long_kernel(Pre
 // 64-key tiles each (68 KB of LDS), so that while one block waits (its
 // start, its gathers, the dispatch of the next block) the other computes.
 // At tile t the wave waits for all its copies and a barrier makes everyone's
-// visible (K of t+1, V of t, issued in tile t-1, and the ids of t+2 for this
-// tile's gathers); then it refills the stages tile t-1 used, K of t+2 and V of
-// t+1, copies the ids of t+3, and runs units 2t and 2t+1.
+// visible (K of t+1 and V of t, issued in tile t-1); then it refills the
+// stages tile t-1 used, K of t+2 and V of t+1 (from ids it read into
+// registers in tile t-1), copies the ids of t+4, reads the ids of the next
+// tile's gathers, and runs units 2t and 2t+1.
 //
 // Differences from the single-block layout:
 //  - Gathers: wave w's instruction i writes LDS rows 16w + 4i + lane/16, each
