@@ -611,7 +611,57 @@ def ceilings(iters: int) -> int:
                       "GBs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
     del x, y
     read_ceilings(iters, stream)
+    mfma_ceilings(stream)
     return 0
+
+
+def mfma_ceilings(stream) -> None:
+    """Matrix-core ceilings of the prefill kernel's inner loop, from the probe
+    kernel in csrc/probes/mfma_ceilings.hip: 16 bf16 MFMAs (32x32x16) per 32 keys
+    per 32 query columns, with operands from registers, with the kernel's LDS
+    operand reads, and with those plus a softmax-like vector load; 32 or 64
+    columns per wave.  Run on random N(0,1) bf16 data and on zeros: the clock the
+    loop holds (shader cycles over the 100 MHz constant clock, mean over blocks)
+    depends on the data.  mfma_busy = MFMA cycles (32 per instruction, from the
+    dense peak) over elapsed cycles per SIMD.  One JSON line each."""
+    import ctypes
+
+    import torch
+
+    from paged_kv_attention_slots_amd import build as _build
+
+    lib = ctypes.CDLL(_build.PROBES_PATH)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.msglp_mfma_loop.argtypes = [I, I, P, I, I, P, P, P]
+    dev = stream.device
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(5)
+    data = {"random": torch.randn(16384, generator=gen).to(torch.bfloat16).to(dev),
+            "zero": torch.zeros(16384, dtype=torch.bfloat16, device=dev)}
+    units = 2000
+    names = {0: "MFMA only (operands in registers)", 1: "MFMA + LDS operand reads",
+             2: "MFMA + LDS operand reads + softmax-like VALU"}
+    for dname, src in data.items():
+        for wide, v in ((0, 0), (0, 1), (0, 2), (1, 1), (1, 2)):
+            nc = 2 if wide else 1
+            waves = 4 * nc
+            blocks = (4 if nc == 1 else 2) * cus
+            sink = torch.zeros(blocks * 64 * waves, device=dev)
+            clk = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+            call = lambda: lib.msglp_mfma_loop(v, wide, src.data_ptr(), blocks, units, sink.data_ptr(),
+                                               clk.data_ptr(), stream.cuda_stream)
+            assert call() == 0
+            ms = _time_stream(call, stream, 3, warm=1)
+            c = clk.view(-1, 2).double().cpu()
+            ghz = float((c[:, 0] / (c[:, 1] / 100e6)).mean()) / 1e9
+            mfmas = blocks * waves * units * 16 * nc
+            tf = mfmas * 32768 / (ms * 1e-3) / 1e12
+            busy = mfmas * 32 / (4 * cus) / (ms * 1e-3 * ghz * 1e9)
+            print(json.dumps({"ceiling": names[v], "query_columns_per_wave": 32 * nc, "data": dname,
+                              "ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                              "frac_bf16_peak": round(tf / BF16_DENSE_PEAK_TFLOPS, 4),
+                              "clock_GHz": round(ghz, 3), "mfma_busy": round(busy, 3)}), flush=True)
 
 
 def read_ceilings(iters: int, stream) -> None:
