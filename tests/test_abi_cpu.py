@@ -210,3 +210,25 @@ def test_binding_refuses_host_tensors(L):
     x = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         L.msgl_store_kv(x, x, x[:1], x[:1], torch.zeros(1, dtype=torch.int32))
+
+
+def test_measurement_probes_exported():
+    """The bench's ceiling probes (a separate library, never linked into the
+    product) load and reject malformed calls before any launch."""
+    from paged_kv_attention_slots_amd import build as _build
+
+    if not os.path.exists(_build.PROBES_PATH):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(_build.PROBES_PATH)
+    for n in ("msglp_stream_read", "msglp_gather_heads", "msglp_mfma_loop"):
+        assert hasattr(lib, n), n
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.msglp_mfma_loop.argtypes = [I, I, P, I, I, P, P, P]
+    lib.msglp_stream_read.argtypes = [P, I64, P, I, P]
+    invalid = 1  # hipErrorInvalidValue
+    assert lib.msglp_mfma_loop(0, 0, None, 0, 10, None, None, None) == invalid  # no blocks
+    assert lib.msglp_mfma_loop(3, 0, None, 1, 10, None, None, None) == invalid  # unknown variant
+    assert lib.msglp_mfma_loop(0, 0, None, 1, 0, None, None, None) == invalid   # no units
+    assert lib.msglp_stream_read(None, 15, None, 1, None) == invalid            # not a multiple of 16
+    product = ctypes.CDLL(_build.LIB_PATH)
+    assert not hasattr(product, "msglp_mfma_loop") and not hasattr(product, "msglp_stream_read")
