@@ -382,6 +382,44 @@ msgl_status msgl_validate_batch(const int32_t *page_table, int32_t rows, int32_t
                                 const int32_t *out_loc, int32_t num_tokens, int64_t dummy_slot);
 
 /*
+ * msgl_check_batch - the checks of msgl_validate_batch, run on the DEVICE
+ * arrays as kernels on `stream`: no host copy, no allocation, no
+ * synchronisation, so a debug build of an engine can run (or capture) it right
+ * before its attention calls.  The invariants are those of the engine's
+ * per-batch metadata (Mini-SGLang tag page, Engine article, the metadata
+ * step: keys page_table[table_idx[b], 0 .. seq_lens[b]-1], new tokens the
+ * entries from cached_lens[b] on, out_loc listing them in request order;
+ * KV-cache article: pages of page_size consecutive slots).
+ * Arguments as for msgl_validate_batch, all arrays in device memory, plus:
+ *   result  device int32 [4], written by the call: [0] the OR of the
+ *           MSGL_CHECK_* codes found (0: none), [1] the number of requests
+ *           with a violation, [2] the first such request, [3] the first new
+ *           token whose out_loc entry fails (INT32_MAX when none);
+ *   seen    NULL, or device uint32 scratch of ceil(num_slots / 32) words for
+ *           the repeat check of out_loc (cleared by the call; NULL skips it).
+ * out_loc with cached_lens needs cu_q (the new tokens' offsets); without
+ * cached_lens (decode) out_loc must have batch entries, one per request.
+ * Every kernel read stays in bounds whatever the metadata hold.  The result is
+ * ready when the stream reaches it; a call that overlaps another one sharing
+ * `result` or `seen` races with it.  Returns MSGL_INVALID_ARG for NULL
+ * required pointers or bad scalars, MSGL_UNSUPPORTED for num_slots >= 2^31.
+ */
+#define MSGL_CHECK_TABLE_IDX 1     /* table_idx[b] outside [0, rows) */
+#define MSGL_CHECK_SEQ_LEN 2       /* seq_lens[b] outside [1, min(max_seq_len, row_stride)] */
+#define MSGL_CHECK_CACHED_LEN 4    /* cached_lens[b] outside [0, seq_lens[b]) */
+#define MSGL_CHECK_CU_Q 8          /* cu_q[0] != 0, or cu_q[b+1] - cu_q[b] != seq_lens[b] - cached_lens[b] */
+#define MSGL_CHECK_SLOT 16         /* a page-table entry the request uses outside [0, num_slots) */
+#define MSGL_CHECK_PAGE 32         /* page_size > 1: a page not made of consecutive slots from a multiple of page_size */
+#define MSGL_CHECK_OUT_LOC 64      /* out_loc[t] outside [0, num_slots) or not page_table[row, position] */
+#define MSGL_CHECK_REPEAT 128      /* out_loc repeats a slot other than dummy_slot */
+#define MSGL_CHECK_TOKEN_COUNT 256 /* cu_q[batch] != num_tokens, or a new token indexed outside out_loc */
+msgl_status msgl_check_batch(const int32_t *page_table, int32_t rows, int32_t row_stride,
+                             const int32_t *table_idx, const int32_t *seq_lens, const int32_t *cached_lens,
+                             const int32_t *cu_q, int32_t batch, int32_t max_seq_len, int64_t num_slots,
+                             int32_t page_size, const int32_t *out_loc, int32_t num_tokens, int64_t dummy_slot,
+                             int32_t *result, uint32_t *seen, void *stream);
+
+/*
  * msgl_validate_shared_prefix - check the group metadata of
  * msgl_decode_attn_shared_prefix on HOST copies (the preconditions listed
  * there).  Returns MSGL_OK or MSGL_INVALID_ARG with the first violation in

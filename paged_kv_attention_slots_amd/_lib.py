@@ -34,8 +34,12 @@ EXPORTS = (
     "msgl_decode_attn", "msgl_decode_attn_noalloc", "msgl_noalloc_scratch_bytes", "msgl_prefill_attn",
     "msgl_decode_graph_create", "msgl_graph_launch", "msgl_graph_destroy", "msgl_validate_batch", "msgl_decode_shared_prefix_workspace_bytes",
     "msgl_decode_attn_shared_prefix", "msgl_validate_shared_prefix", "msgl_prefill_plan_bytes",
-    "msgl_prefill_plan", "msgl_prefill_attn_planned",
+    "msgl_prefill_plan", "msgl_prefill_attn_planned", "msgl_check_batch",
 )
+
+# msgl_check_batch codes (include/msgl.h MSGL_CHECK_*)
+CHECK_CODES = {"table_idx": 1, "seq_len": 2, "cached_len": 4, "cu_q": 8, "slot": 16, "page": 32,
+               "out_loc": 64, "repeat": 128, "token_count": 256}
 
 
 class MsglError(RuntimeError):
@@ -96,6 +100,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msgl_graph_destroy.argtypes = [P]
     lib.msgl_validate_batch.restype = st
     lib.msgl_validate_batch.argtypes = [P, I32, I32, P, P, P, P, I32, I32, I64, I32, P, I32, I64]
+    lib.msgl_check_batch.restype = st
+    lib.msgl_check_batch.argtypes = [P, I32, I32, P, P, P, P, I32, I32, I64, I32, P, I32, I64, P, P, P]
     return lib
 
 
@@ -356,3 +362,23 @@ def msgl_validate_batch(page_table, table_idx, seq_lens, cached_lens, cu_q, max_
                                    c(table_idx), c(seq_lens), c(cached_lens), c(cu_q),
                                    table_idx.numel(), max_seq_len, num_slots, page_size, c(out_loc),
                                    0 if out_loc is None else out_loc.numel(), dummy_slot))
+
+
+def msgl_check_batch(page_table, table_idx, seq_lens, cached_lens, cu_q, max_seq_len: int, num_slots: int,
+                     page_size: int = 1, out_loc=None, dummy_slot: int = -1, result=None, seen=None,
+                     stream=None) -> torch.Tensor:
+    """Enqueue the device-side metadata check on GPU tensors; returns the int32
+    [4] result tensor (codes, flagged requests, first request, first token),
+    valid once the stream reaches it.  seen: optional int32 scratch of
+    ceil(num_slots / 32) words for the out_loc repeat check."""
+    dev = page_table.device
+    if result is None:
+        result = torch.empty(4, dtype=torch.int32, device=dev)
+    if seen is not None and seen.numel() < (num_slots + 31) // 32:
+        raise ValueError("seen holds fewer than ceil(num_slots / 32) words")
+    c = lambda t: None if t is None else _p(_i32(t))
+    _check(lib.msgl_check_batch(c(page_table), page_table.shape[0], page_table.shape[1], c(table_idx),
+                                c(seq_lens), c(cached_lens), c(cu_q), table_idx.numel(), max_seq_len, num_slots,
+                                page_size, c(out_loc), 0 if out_loc is None else out_loc.numel(), dummy_slot,
+                                c(result), c(seen), _stream(stream)))
+    return result

@@ -685,6 +685,41 @@ msgl_status msgl_validate_shared_prefix(const int32_t *page_table, int32_t rows,
     return ok();
 }
 
+msgl_status msgl_check_batch(const int32_t *page_table, int32_t rows, int32_t row_stride,
+                             const int32_t *table_idx, const int32_t *seq_lens, const int32_t *cached_lens,
+                             const int32_t *cu_q, int32_t batch, int32_t max_seq_len, int64_t num_slots,
+                             int32_t page_size, const int32_t *out_loc, int32_t num_tokens, int64_t dummy_slot,
+                             int32_t *result, uint32_t *seen, void *stream) {
+    if (!page_table || !table_idx || !seq_lens || !result) return fail(MSGL_INVALID_ARG, "NULL pointer argument");
+    if (rows < 1 || row_stride < 1 || batch < 0 || max_seq_len < 1 || num_slots < 1 || page_size < 1 ||
+        num_tokens < 0)
+        return fail(MSGL_INVALID_ARG, "bad scalar argument");
+    if (out_loc && !cu_q && cached_lens)
+        return fail(MSGL_INVALID_ARG, "checking out_loc of a batch with cached_lens needs cu_q");
+    if (out_loc && !cu_q && num_tokens != batch)
+        return fail(MSGL_INVALID_ARG, "out_loc of a decode batch has %d entries for %d requests", num_tokens, batch);
+    if (num_slots > INT32_MAX) return fail(MSGL_UNSUPPORTED, "num_slots %lld above 2^31 - 1", (long long)num_slots);
+    msgl::CheckBatchArgs a;
+    a.page_table = page_table;
+    a.rows = rows;
+    a.row_stride = row_stride;
+    a.table_idx = table_idx;
+    a.seq_lens = seq_lens;
+    a.cached_lens = cached_lens;
+    a.cu_q = cu_q;
+    a.batch = batch;
+    a.max_seq_len = max_seq_len;
+    a.num_slots = num_slots;
+    a.page_size = page_size;
+    a.out_loc = out_loc;
+    a.num_tokens = num_tokens;
+    a.dummy_slot = dummy_slot;
+    a.result = result;
+    a.seen = out_loc ? seen : nullptr;
+    a.seen_words = a.seen ? (num_slots + 31) / 32 : 0;
+    return from_hip(msgl::launch_check_batch(a, static_cast<hipStream_t>(stream)), "check_batch launch");
+}
+
 msgl_status msgl_validate_batch(const int32_t *page_table, int32_t rows, int32_t row_stride,
                                 const int32_t *table_idx, const int32_t *seq_lens,
                                 const int32_t *cached_lens, const int32_t *cu_q, int32_t batch,

@@ -206,6 +206,36 @@ def test_validate_batch(L):
                               num_slots=w.num_slots_total, page_size=1)
 
 
+def test_check_batch_argument_checks(L):
+    """msgl_check_batch refuses NULL required pointers, bad scalars and
+    out_loc checks it cannot place, before any launch."""
+    lib = ctypes.CDLL(L.LIB_PATH)
+    f = lib.msgl_check_batch
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    f.argtypes = [P, I32, I32, P, P, P, P, I32, I32, I64, I32, P, I32, I64, P, P, P]
+    FAKE = 4096  # never dereferenced: every call below fails its host checks first
+    ok_args = [FAKE, 4, 64, FAKE, FAKE, None, None, 4, 64, 1000, 1, None, 0, -1, FAKE, None, None]
+
+    def call(**kw):
+        a = list(ok_args)
+        names = ["page_table", "rows", "row_stride", "table_idx", "seq_lens", "cached_lens", "cu_q", "batch",
+                 "max_seq_len", "num_slots", "page_size", "out_loc", "num_tokens", "dummy_slot", "result", "seen",
+                 "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(page_table=None) == L.MSGL_INVALID_ARG
+    assert call(result=None) == L.MSGL_INVALID_ARG and "NULL" in L.msgl_last_error()
+    assert call(rows=0) == L.MSGL_INVALID_ARG
+    assert call(page_size=0) == L.MSGL_INVALID_ARG
+    assert call(num_tokens=-1) == L.MSGL_INVALID_ARG
+    assert call(out_loc=FAKE, cached_lens=FAKE, num_tokens=4) == L.MSGL_INVALID_ARG
+    assert "cu_q" in L.msgl_last_error()
+    assert call(out_loc=FAKE, num_tokens=3) == L.MSGL_INVALID_ARG and "decode" in L.msgl_last_error()
+    assert call(num_slots=1 << 31) == L.MSGL_UNSUPPORTED
+
+
 def test_binding_refuses_host_tensors(L):
     x = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
