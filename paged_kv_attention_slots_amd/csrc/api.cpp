@@ -15,6 +15,7 @@
 
 #include "../../include/msgl.h"
 #include "launch.h"
+#include "check_batch.h"
 
 namespace {
 

@@ -19,7 +19,7 @@
 #include <climits>
 
 #include "common.h"
-#include "launch.h"
+#include "check_batch.h"
 
 namespace msgl {
 
