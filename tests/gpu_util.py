@@ -40,22 +40,24 @@ def max_abs(out_gpu: torch.Tensor, ref: torch.Tensor) -> float:
 
 def rowsum_error(w, kp_ref, vp_ref, lse_gpu: torch.Tensor, requests: Sequence[int]) -> float:
     """max |sum_j exp(s_j - lse) - 1| over the given requests' query rows and
-    heads, with s_j recomputed in fp64 on the host from the post-store pool."""
+    heads, with s_j recomputed in fp64 on the host from the post-store pool
+    (q head h reads kv head h // (H / G))."""
     lse = lse_gpu.detach().cpu().to(torch.float64)
     H, G, d = w.q_heads, w.kv_heads, w.head_dim
     g = H // G
     worst = 0.0
     q = w.q.detach().cpu().to(torch.float64)
+    seq_lens, cu_q, table_idx = w.seq_lens.cpu(), w.cu_q.cpu(), w.table_idx.cpu()
+    page_table = w.page_table.cpu()
     for b in requests:
-        L = int(w.seq_lens[b])
-        c0, c1 = int(w.cu_q[b]), int(w.cu_q[b + 1])
-        row = w.page_table[int(w.table_idx[b]), :L].cpu().long()
+        L = int(seq_lens[b])
+        c0, c1 = int(cu_q[b]), int(cu_q[b + 1])
+        row = page_table[int(table_idx[b]), :L].long()
         K = kp_ref[row].to(torch.float64)  # [L, G, d]
         for t in range(c0, c1):
             p = L - (c1 - c0) + (t - c0)
-            Kh = K[:p + 1].repeat_interleave(g, dim=1)  # [p+1, H, d]
-            s = torch.einsum("jhd,hd->hj", Kh, q[t]) / math.sqrt(d)
-            tot = torch.exp(s - lse[t][:, None]).sum(dim=1)
+            s = torch.einsum("jgd,gkd->gkj", K[:p + 1], q[t].view(G, g, d)) / math.sqrt(d)  # [G, g, p+1]
+            tot = torch.exp(s - lse[t].view(G, g, 1)).sum(dim=2)
             worst = max(worst, float((tot - 1.0).abs().max()))
     return worst
 

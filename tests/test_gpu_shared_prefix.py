@@ -39,7 +39,7 @@ def _run(L, runner, sp, chunk=0):
     return out, lse, out_d
 
 
-def _check(oracle_mod, mods, sp, rowsum_reqs, chunk=0):
+def _check(oracle_mod, mods, sp, chunk=0):
     L, runner, _ = mods
     w = sp.w
     say(f"[shared] {w.name} bs={w.bs} groups={sp.group_start.numel() - 1} max_prefix={sp.max_prefix_len} "
@@ -49,7 +49,7 @@ def _check(oracle_mod, mods, sp, rowsum_reqs, chunk=0):
     err = max_abs(out, out_ref)
     err_d = max_abs(out, out_d.double().cpu())
     lse_err = max_abs(lse, lse_ref)
-    rs = rowsum_error(w, kp, vp, lse, rowsum_reqs)
+    rs = rowsum_error(w, kp, vp, lse, range(w.bs))  # every request
     say(f"[shared] {w.name}: max-abs {err:.3e} (plain decode {err_d:.3e}), lse {lse_err:.2e}, rowsum {rs:.2e}")
     assert err <= BF16_TOL and err_d <= BF16_TOL, (err, err_d)
     assert lse_err < 1e-3, lse_err
@@ -58,14 +58,14 @@ def _check(oracle_mod, mods, sp, rowsum_reqs, chunk=0):
 
 def test_four_groups_of_64_on_4096(oracle_mod, mods):
     _, _, wl = mods
-    _check(oracle_mod, mods, wl.shared_prefix_decode(device="cuda"), rowsum_reqs=range(0, 256, 37))
+    _check(oracle_mod, mods, wl.shared_prefix_decode(device="cuda"))
 
 
 def test_sharp_queries(oracle_mod, mods):
     _, _, wl = mods
     sp = wl.shared_prefix_decode(device="cuda", group_sizes=(32, 16), prefixes=(3000, 1500), singles=8,
                                  q_std=1.0, num_slots=1 << 18)
-    _check(oracle_mod, mods, sp, rowsum_reqs=range(0, 56, 5))
+    _check(oracle_mod, mods, sp)
 
 
 def test_page_size_16_uneven_groups(oracle_mod, mods):
@@ -74,7 +74,7 @@ def test_page_size_16_uneven_groups(oracle_mod, mods):
     _, _, wl = mods
     sp = wl.shared_prefix_decode(device="cuda", group_sizes=(40, 64, 16, 8), prefixes=(4096, 2048, 1024, 8192),
                                  page_size=16, num_slots=1 << 20)
-    _check(oracle_mod, mods, sp, rowsum_reqs=range(0, 128, 13))
+    _check(oracle_mod, mods, sp)
 
 
 def test_ragged_prefixes_singletons_gqa2(oracle_mod, mods):
@@ -83,13 +83,13 @@ def test_ragged_prefixes_singletons_gqa2(oracle_mod, mods):
     _, _, wl = mods
     sp = wl.shared_prefix_decode(device="cuda", group_sizes=(70, 1, 5, 1), prefixes=(1000, 77, 130, 1),
                                  singles=6, heads=wl.QWEN3_06B, num_slots=1 << 18, suffix_lo=1, suffix_hi=300)
-    _check(oracle_mod, mods, sp, rowsum_reqs=range(0, 83, 7))
+    _check(oracle_mod, mods, sp)
 
 
 def test_no_shared_prefix_is_plain_decode(oracle_mod, mods):
     _, _, wl = mods
     sp = wl.shared_prefix_decode(device="cuda", group_sizes=(), prefixes=(), singles=24, num_slots=1 << 16)
-    _check(oracle_mod, mods, sp, rowsum_reqs=range(24))
+    _check(oracle_mod, mods, sp)
 
 
 @pytest.mark.parametrize("chunk", [64, 512])
@@ -97,7 +97,7 @@ def test_decode_split_sizes(oracle_mod, mods, chunk):
     _, _, wl = mods
     sp = wl.shared_prefix_decode(device="cuda", group_sizes=(20, 12), prefixes=(2500, 640), singles=3,
                                  num_slots=1 << 17)
-    _check(oracle_mod, mods, sp, rowsum_reqs=range(0, 35, 4), chunk=chunk)
+    _check(oracle_mod, mods, sp, chunk=chunk)
 
 
 @pytest.mark.parametrize("H,G", [(8, 8), (64, 8)])
@@ -106,4 +106,4 @@ def test_group_sizes_one_and_eight(oracle_mod, mods, H, G):
     _, _, wl = mods
     sp = wl.shared_prefix_decode(device="cuda", group_sizes=(40, 9), prefixes=(1500, 700), singles=2,
                                  heads=dict(H=H, G=G, d=128), num_slots=1 << 17, q_std=1.0)
-    _check(oracle_mod, mods, sp, rowsum_reqs=range(0, 51, 6))
+    _check(oracle_mod, mods, sp)
