@@ -192,3 +192,38 @@ def test_random_corruptions_agree_with_host(mods):
             flagged += r[0] != 0
     say(f"[check] random corruptions: {agree} agree with the host validator, {flagged} flagged")
     assert flagged >= agree // 4
+
+
+def test_check_batch_under_graph_capture(mods):
+    """The check records into a captured graph (kernels only, no memset) and
+    each replay re-checks whatever the recorded buffers hold."""
+    L, wl = mods
+    w = wl.ragged_prefill(device="cuda", n_req=6, e_lo=20, e_hi=90, c_lo=0, c_hi=70, num_slots=4096)
+    m = _meta(w)
+    g_ = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in m.items()}
+    result = torch.empty(4, dtype=torch.int32, device="cuda")
+    seen = torch.empty((m["num_slots"] + 31) // 32, dtype=torch.int32, device="cuda")
+    st = torch.cuda.Stream()
+    call = lambda: L.msgl_check_batch(g_["page_table"], g_["table_idx"], g_["seq_lens"], g_["cached_lens"],
+                                      g_["cu_q"], m["max_seq_len"], m["num_slots"], m["page_size"],
+                                      out_loc=g_["out_loc"], dummy_slot=m["dummy_slot"], result=result, seen=seen,
+                                      stream=st)
+    with torch.cuda.stream(st):
+        call()  # eager once before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        call()
+    torch.cuda.synchronize()
+    good = list(g_["seq_lens"].cpu())
+    for rnd in range(3):
+        result.fill_(7)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert [int(x) for x in result.cpu()] == [0, 0, INT_MAX, INT_MAX], rnd
+        g_["seq_lens"][2] = 0  # a violation planted in the recorded buffer
+        graph.replay()
+        torch.cuda.synchronize()
+        r = [int(x) for x in result.cpu()]
+        assert r[0] & L.CHECK_CODES["seq_len"] and r[2] == 2, (rnd, r)
+        g_["seq_lens"][2] = int(good[2])
