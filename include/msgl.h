@@ -14,7 +14,7 @@
  * --------------------------------
  * Pointers named *_pool, q, q_out, out, lse, k_new, v_new, page_table, table_idx,
  * seq_lens, cached_lens, cu_q, positions, out_loc, weight, ids, group_start,
- * prefix_lens and workspace are DEVICE pointers owned
+ * prefix_lens, workspace, result and seen are DEVICE pointers owned
  * by the caller; the library never frees or retains them (except a captured
  * graph, which records them; see msgl_decode_graph_create).  `stream` is a
  * hipStream_t passed as void* (NULL = the null stream).  Calls only enqueue
@@ -41,7 +41,10 @@
  *
  * Preconditions on device-array contents are not checked by the compute calls
  * (checking them would need a host synchronisation); msgl_validate_batch
- * checks host copies.  Only host scalars and pointer presence are validated;
+ * checks host copies, and msgl_check_batch checks the device arrays
+ * themselves, asynchronously, into a device result (a debug step that can run
+ * or be captured before the attention calls).  Only host scalars and pointer
+ * presence are validated;
  * a bad value returns a status and enqueues nothing.  The kernels clamp the
  * slot ids and lengths they read into range, but table_idx is a pure
  * precondition (0 <= table_idx[b] < the page table's rows, a count the
