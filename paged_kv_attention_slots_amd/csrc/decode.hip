@@ -29,8 +29,6 @@
 
 namespace msgl {
 
-// Work units a request costs beyond its keys (see above).
-constexpr int kPieceUnits = 32;
 // Batches up to this size merge with four waves per (request, q head).
 constexpr int kMergeSplitBatch = 64;
 
@@ -340,6 +338,19 @@ int device_cu_count() {
     return cached[dev];
 }
 
+// Waves (kv heads) per decode block: the largest power of two up to
+// kDecodeWaves that divides kv_heads.
+int decode_waves(int kv_heads) {
+#ifdef MSGL_DECODE_WPB  // tuning builds only
+    constexpr int kDecodeWaves = MSGL_DECODE_WPB;
+#else
+    constexpr int kDecodeWaves = 4;
+#endif
+    int w = kDecodeWaves;
+    while (w > 1 && kv_heads % w != 0) w >>= 1;
+    return w;
+}
+
 namespace {
 
 // Loads per wave-iteration of the decode pipeline (4 tokens per load for
@@ -370,22 +381,10 @@ int decode_occupancy(int threads, int batch) {
 }
 
 // prepare_only: resolve the cached device queries (CU count, occupancy) and
-// launch nothing; used before stream capture.
-// Waves (kv heads) per decode block: the largest power of two up to
-// kDecodeWaves that divides kv_heads.
-int decode_waves(int kv_heads) {
-#ifdef MSGL_DECODE_WPB  // tuning builds only
-    constexpr int kDecodeWaves = MSGL_DECODE_WPB;
-#else
-    constexpr int kDecodeWaves = 4;
-#endif
-    int w = kDecodeWaves;
-    while (w > 1 && kv_heads % w != 0) w >>= 1;
-    return w;
-}
-
+// launch nothing; used before stream capture.  split_only: the split kernel
+// alone (the cascade merges the pieces itself).
 template <typename T, int D, int GQ>
-hipError_t run_decode(const DecodeArgs &a_in, hipStream_t stream, bool prepare_only) {
+hipError_t run_decode(const DecodeArgs &a_in, hipStream_t stream, bool prepare_only, bool split_only) {
     DecodeArgs a = a_in;
     a.wpb = decode_waves(a.kv_heads);
     const int threads = 64 * a.wpb;
@@ -402,7 +401,7 @@ hipError_t run_decode(const DecodeArgs &a_in, hipStream_t stream, bool prepare_o
     hipLaunchKernelGGL((decode_split_kernel<T, D, GQ, decode_unroll<T, D>()>), dim3((unsigned)grid),
                        dim3(threads), smem, stream, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || split_only) return e;
     if (a.batch <= kMergeSplitBatch)
         hipLaunchKernelGGL((decode_merge_kernel<T, D, GQ, 4>), dim3(a.batch, a.q_heads), dim3(256), 0, stream, a);
     else
@@ -412,12 +411,12 @@ hipError_t run_decode(const DecodeArgs &a_in, hipStream_t stream, bool prepare_o
 }
 
 template <typename T, int D>
-hipError_t run_decode_g(const DecodeArgs &a, hipStream_t stream, bool prep) {
+hipError_t run_decode_g(const DecodeArgs &a, hipStream_t stream, bool prep, bool split_only) {
     switch (a.q_heads / a.kv_heads) {
-        case 1: return run_decode<T, D, 1>(a, stream, prep);
-        case 2: return run_decode<T, D, 2>(a, stream, prep);
-        case 4: return run_decode<T, D, 4>(a, stream, prep);
-        case 8: return run_decode<T, D, 8>(a, stream, prep);
+        case 1: return run_decode<T, D, 1>(a, stream, prep, split_only);
+        case 2: return run_decode<T, D, 2>(a, stream, prep, split_only);
+        case 4: return run_decode<T, D, 4>(a, stream, prep, split_only);
+        case 8: return run_decode<T, D, 8>(a, stream, prep, split_only);
         default: return hipErrorInvalidValue;
     }
 }
@@ -432,13 +431,13 @@ size_t decode_workspace_bytes(int batch, int q_heads, int head_dim, int max_seq_
 }
 
 hipError_t launch_decode(const DecodeArgs &a, DType dtype, int head_dim, hipStream_t stream,
-                         bool prepare_only) {
+                         bool prepare_only, bool split_only) {
     if (dtype == kBF16) {
-        if (head_dim == 128) return run_decode_g<bf16_t, 128>(a, stream, prepare_only);
-        if (head_dim == 64) return run_decode_g<bf16_t, 64>(a, stream, prepare_only);
+        if (head_dim == 128) return run_decode_g<bf16_t, 128>(a, stream, prepare_only, split_only);
+        if (head_dim == 64) return run_decode_g<bf16_t, 64>(a, stream, prepare_only, split_only);
     } else {
-        if (head_dim == 128) return run_decode_g<float, 128>(a, stream, prepare_only);
-        if (head_dim == 64) return run_decode_g<float, 64>(a, stream, prepare_only);
+        if (head_dim == 128) return run_decode_g<float, 128>(a, stream, prepare_only, split_only);
+        if (head_dim == 64) return run_decode_g<float, 64>(a, stream, prepare_only, split_only);
     }
     return hipErrorInvalidValue;
 }

@@ -15,6 +15,8 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 constexpr int kDefaultChunk = 64;
 // Bytes of the decode workspace's control block.
 constexpr size_t kCtrlBytes = 256;
+// Work units a decode request costs beyond its keys (the split's fixed cost per piece).
+constexpr int kPieceUnits = 32;
 // Upper bound of the decode grid (it sizes the workspace's partial states).
 constexpr int kMaxDecodeGrid = 4096;
 
@@ -167,9 +169,13 @@ hipError_t launch_store_kv(const StoreKvArgs &a, hipStream_t stream);
 hipError_t launch_rope_store_kv(const RopeStoreKvArgs &a, DType dtype, hipStream_t stream);
 hipError_t launch_vocab_embed(const VocabEmbedArgs &a, hipStream_t stream);
 // prepare_only resolves the cached device queries and launches nothing (call
-// it before capturing the launch into a graph).
+// it before capturing the launch into a graph); split_only launches the split
+// kernel alone, leaving the pieces of requests cut across blocks in the
+// workspace for a merge of the caller's (the cascade's).
 hipError_t launch_decode(const DecodeArgs &a, DType dtype, int head_dim, hipStream_t stream,
-                         bool prepare_only = false);
+                         bool prepare_only = false, bool split_only = false);
+// Kv heads per decode block.
+int decode_waves(int kv_heads);
 // bf16 prefill on matrix cores when the shape is supported, else the VALU path.
 hipError_t launch_prefill(const PrefillArgs &a, DType dtype, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_valu(const PrefillArgs &a, DType dtype, int head_dim, hipStream_t stream);

@@ -36,6 +36,14 @@ struct CascadeMergeArgs {
     int32_t batch;
     int32_t q_heads;
     int32_t splits;             // 0 when the prefix pass did not run
+    // the suffix pass's split kernel: a request whose own keys were cut across
+    // blocks left its pieces' unnormalised states here instead of an output
+    const int64_t *ctrl;        // [2] total work units, units per block
+    const int32_t *prefix;      // [batch + 1] work units before each request
+    const float *part_o;        // [batch + grid, q_heads, D] unnormalised outputs
+    const float *part_ml;       // [batch + grid, q_heads, 2] (max in log2 units, sum)
+    int32_t group;              // q heads per kv head
+    int32_t wpb;                // kv heads per decode block
 };
 
 namespace {
@@ -58,7 +66,10 @@ MSGL_DEV float lanes_sum(float x) {
 // reads split s's lse, so the weights take one round trip; the splits' partial
 // outputs are then read with every split's loads in flight at once (the loop
 // over kMaxPrefixSplits is unrolled).  An empty split (lse = -inf) was never
-// written and is skipped.
+// written and is skipped.  The suffix is either the split kernel's normalised
+// output and lse, or, for a request whose own keys were cut across decode
+// blocks, its pieces' unnormalised states (the decode merge's inputs), which
+// enter the same log-sum-exp sum directly: no separate decode merge runs.
 template <int D>
 __global__ __launch_bounds__(256) void cascade_merge_kernel(CascadeMergeArgs a) {
     constexpr int PER = D / 64;
@@ -70,16 +81,35 @@ __global__ __launch_bounds__(256) void cascade_merge_kernel(CascadeMergeArgs a) 
     const int64_t bh = (int64_t)b * a.q_heads + h;
     const int S = a.prefix_lens[b] > 0 ? min(a.splits, kMaxPrefixSplits) : 0;
     const int64_t sstride = (int64_t)a.batch * a.q_heads;
-    const float xs = a.suffix_lse[bh];
+    // the suffix's pieces: n > 1 when the split kernel cut this request's own keys across blocks
+    const int W = a.prefix[b + 1] - a.prefix[b];
+    const int L = W - kPieceUnits;
+    int n = 1;
+    int64_t i0 = 0;
+    if (L > 1) {
+        const int64_t total = a.ctrl[0], share = a.ctrl[1];
+        const int hg = (h / a.group) / a.wpb;
+        const int64_t first_tok = (int64_t)hg * total + a.prefix[b] + kPieceUnits;
+        const int first = (int)(first_tok / share);
+        n = (int)((first_tok + L - 1) / share) - first + 1;
+        i0 = ((int64_t)b + first) * a.q_heads + h;  // piece k at (i0 + k q_heads)
+    }
+    // reference: the largest lse of the splits, the suffix or its pieces (natural log)
     const float x = lane < S ? a.prefix_lse[lane * sstride + bh] : -INFINITY;
-    const float m = fmaxf(lanes_max(x), xs);
+    float m = x;
+    const float xs = n == 1 ? a.suffix_lse[bh] : -INFINITY;
+    for (int k = lane; n > 1 && k < n; k += 64) {
+        const float2 v = *reinterpret_cast<const float2 *>(a.part_ml + (i0 + (int64_t)k * a.q_heads) * 2);
+        m = fmaxf(m, (v.x + __log2f(v.y)) * kLn2);
+    }
+    m = fmaxf(lanes_max(m), xs);
     const float wx = x == -INFINITY ? 0.0f : expf(x - m);
-    const float ws = expf(xs - m);
-    const float l = lanes_sum(wx) + ws;
+    const float ws = n == 1 ? expf(xs - m) : 0.0f;
     const uint64_t live = __ballot(x != -INFINITY);
+    float l = wx;
     float acc[PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = ws * a.suffix_o[bh * D + lane * PER + e];
+    for (int e = 0; e < PER; ++e) acc[e] = n == 1 ? ws * a.suffix_o[bh * D + lane * PER + e] : 0.0f;
 #pragma unroll
     for (int s = 0; s < kMaxPrefixSplits; ++s) {
         const float w = __shfl(wx, s);
@@ -89,6 +119,25 @@ __global__ __launch_bounds__(256) void cascade_merge_kernel(CascadeMergeArgs a) 
             for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[e], acc[e]);
         }
     }
+    // a piece k weighs 2^(m_k - m log2 e) on its unnormalised output and its sum
+    const float m2 = m * kLog2e;
+    for (int c0 = 0; n > 1 && c0 < n; c0 += 64) {
+        const int k = c0 + lane;
+        float wk = 0.0f;
+        if (k < n) {
+            const float2 v = *reinterpret_cast<const float2 *>(a.part_ml + (i0 + (int64_t)k * a.q_heads) * 2);
+            wk = fast_exp2(v.x - m2);
+            l = fmaf(wk, v.y, l);
+        }
+        const int cn = min(64, n - c0);
+        for (int t = 0; t < cn; ++t) {
+            const float w = __shfl(wk, t);
+            const float *po = a.part_o + (i0 + (int64_t)(c0 + t) * a.q_heads) * D + lane * PER;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[e], acc[e]);
+        }
+    }
+    l = lanes_sum(l) + ws;
     const float inv = 1.0f / l;
     bf16_t *op = a.out + bh * D + lane * PER;
     if constexpr (PER == 2) {
@@ -167,7 +216,7 @@ hipError_t launch_decode_shared_prefix(const SharedPrefixArgs &sp, const DecodeA
         hipError_t e = launch_prefill_shared(p, stream);
         if (e != hipSuccess) return e;
     }
-    hipError_t e = launch_decode(dec, kBF16, head_dim, stream, false);
+    hipError_t e = launch_decode(dec, kBF16, head_dim, stream, false, true);
     if (e != hipSuccess) return e;
     CascadeMergeArgs m;
     m.out = static_cast<bf16_t *>(dec_in.out);
@@ -180,6 +229,12 @@ hipError_t launch_decode_shared_prefix(const SharedPrefixArgs &sp, const DecodeA
     m.batch = dec.batch;
     m.q_heads = dec.q_heads;
     m.splits = splits;
+    m.ctrl = dec.ctrl;
+    m.prefix = dec.prefix;
+    m.part_o = dec.part_o;
+    m.part_ml = dec.part_ml;
+    m.group = dec.q_heads / dec.kv_heads;
+    m.wpb = decode_waves(dec.kv_heads);
     hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(dec.batch, (dec.q_heads + 3) / 4), dim3(256), 0, stream, m);
     return hipGetLastError();
 }
