@@ -641,9 +641,9 @@ def mfma_ceilings(stream) -> None:
             "zero": torch.zeros(16384, dtype=torch.bfloat16, device=dev)}
     units = 2000
     names = {0: "MFMA only (operands in registers)", 1: "MFMA + LDS operand reads",
-             2: "MFMA + LDS operand reads + softmax-like VALU"}
+             2: "MFMA + LDS operand reads + softmax-like VALU", 3: "MFMA only, 16x16x32 (operands in registers)"}
     for dname, src in data.items():
-        for wide, v in ((0, 0), (0, 1), (0, 2), (1, 1), (1, 2)):
+        for wide, v in ((0, 3), (0, 0), (0, 1), (0, 2), (1, 1), (1, 2)):
             nc = 2 if wide else 1
             waves = 4 * nc
             blocks = (4 if nc == 1 else 2) * cus

@@ -169,21 +169,62 @@ __global__ __launch_bounds__(256 * NC, 3 - NC) void mfma_loop(const uint4 *__res
     }
 }
 
+// The matrix cores alone with v_mfma_f32_16x16x32_bf16 (8 independent
+// accumulators, operands from registers, the A/B roles swapped every other
+// pass): the densest issue of the bf16 units, for the power-limited ceiling.
+__global__ __launch_bounds__(256, 2) void mfma16_loop(const uint4 *__restrict__ src, int units, float *sink,
+                                                       unsigned long long *clk, int keep) {
+    typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+    const int lane = threadIdx.x & 63;
+    bf16x8 a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = __builtin_bit_cast(bf16x8, src[(i * 64 + lane) & 2047]);
+        b[i] = __builtin_bit_cast(bf16x8, src[(1024 + i * 64 + lane) & 2047]);
+    }
+    floatx4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = floatx4{};
+    const unsigned long long c0 = __builtin_readcyclecounter(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int u = 0; u < units; ++u) {  // 32 MFMAs of 16384 flops: the flops of one 16-MFMA 32x32x16 unit, twice
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            acc[k & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k & 7], b[(3 * k) & 7], acc[k & 7], 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            acc[k & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[k & 7], a[(5 * k) & 7], acc[k & 7], 0, 0, 0);
+    }
+    const unsigned long long c1 = __builtin_readcyclecounter(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        clk[2 * blockIdx.x] = c1 - c0;
+        clk[2 * blockIdx.x + 1] = r1 - r0;
+    }
+    if (keep) {
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+        sink[blockIdx.x * 256 + threadIdx.x] = t;
+    }
+}
+
 }  // namespace
 
 // Variant v: 0 = matrix cores alone (operands from registers), 1 = with the LDS
-// operand reads, 2 = with LDS reads and the softmax-like vector load; 32 query
+// operand reads, 2 = with LDS reads and the softmax-like vector load, 3 = the
+// matrix cores alone with 16x16x32 MFMAs (32 query columns only); 32 query
 // columns per wave in blocks of 4 waves (two blocks per CU), or, with wide, 64
 // columns per wave in blocks of 8 waves (one block per CU).  src: at least 32 KB
 // of bf16 data; sink: blocks x threads floats (written only with keep);
 // clk: 2 x blocks words.  Returns a hipError_t.
 extern "C" int msglp_mfma_loop(int v, int wide, const void *src, int blocks, int units, float *sink,
                                unsigned long long *clk, void *stream) {
-    if (blocks < 1 || units < 1 || v < 0 || v > 2) return (int)hipErrorInvalidValue;
+    if (blocks < 1 || units < 1 || v < 0 || v > 3 || (v == 3 && wide)) return (int)hipErrorInvalidValue;
     const hipStream_t st = (hipStream_t)stream;
     const uint4 *s = (const uint4 *)src;
     const dim3 g(blocks);
-    if (!wide) {
+    if (v == 3) {  // 16x16x32 MFMAs alone, 4 waves per block: 2 x 16 MFMAs of 16384 flops per unit
+        hipLaunchKernelGGL(mfma16_loop, g, dim3(256), 0, st, s, units, sink, clk, 0);
+    } else if (!wide) {
         const dim3 t(256);
         if (v == 0) hipLaunchKernelGGL((mfma_loop<1, false, false>), g, t, 0, st, s, units, sink, clk, 0);
         if (v == 1) hipLaunchKernelGGL((mfma_loop<1, true, false>), g, t, 0, st, s, units, sink, clk, 0);

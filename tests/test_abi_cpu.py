@@ -257,7 +257,8 @@ def test_measurement_probes_exported():
     lib.msglp_stream_read.argtypes = [P, I64, P, I, P]
     invalid = 1  # hipErrorInvalidValue
     assert lib.msglp_mfma_loop(0, 0, None, 0, 10, None, None, None) == invalid  # no blocks
-    assert lib.msglp_mfma_loop(3, 0, None, 1, 10, None, None, None) == invalid  # unknown variant
+    assert lib.msglp_mfma_loop(4, 0, None, 1, 10, None, None, None) == invalid  # unknown variant
+    assert lib.msglp_mfma_loop(3, 1, None, 1, 10, None, None, None) == invalid  # 16x16x32: 32 columns only
     assert lib.msglp_mfma_loop(0, 0, None, 1, 0, None, None, None) == invalid   # no units
     assert lib.msglp_stream_read(None, 15, None, 1, None) == invalid            # not a multiple of 16
     product = ctypes.CDLL(_build.LIB_PATH)
