@@ -507,20 +507,29 @@ def sweep(iters: int) -> int:
 
 
 def mixed(iters: int) -> int:
+    """The mixed step alone (`--mixed N`): one JSON line."""
+    import torch
+
+    stream = torch.cuda.Stream(device=torch.device("cuda:0"))
+    print(json.dumps(mixed_leg(iters, stream)), flush=True)
+    return 0
+
+
+def mixed_leg(iters: int, stream) -> dict:
     """The mixed multi-layer step (36 layers, 192 decode requests + 2 chunked
     prefills of 2048 on 8192-token prefixes, pool 60% of 288 GB), eager, per
-    layer store_kv -> decode -> prefill.  One JSON line."""
+    layer store_kv -> decode -> prefill, timed over `iters` steps after 4
+    warm-up steps.  Returns its record; the pools are freed on return."""
     import torch
 
     from paged_kv_attention_slots_amd import _lib, workloads as wl
 
-    dev = torch.device("cuda:0")
+    dev = stream.device
     t0 = time.time()
     log("building the mixed step (36 layers, pool 60% of 288 GB)")
     m = wl.mixed_step(device=dev)
     torch.cuda.synchronize()
     log(f"  built in {time.time() - t0:.1f}s")
-    stream = torch.cuda.Stream(device=dev)
     d0, p0 = m.layer_views(0)
     od = torch.empty_like(d0.q)
     op = torch.empty_like(p0.q)
@@ -541,14 +550,15 @@ def mixed(iters: int) -> int:
     sbytes = (2 * 2 * m.num_tokens * d0.kv_heads * d0.head_dim * 2 + 4 * m.num_tokens) * m.layers
     flops = prefill_flops(p0) * m.layers
     roof_ms = ((dbytes + sbytes) / (HBM_PEAK_GBS * 1e9) + flops / (BF16_DENSE_PEAK_TFLOPS * 1e12)) * 1e3
-    print(json.dumps({"mixed_step": "qwen3-8b 36 layers: 192 decode + 2x2048 prefill on 8192 prefix",
-                      "ms_per_step": round(ms, 3), "tokens_per_step": m.num_tokens,
-                      "tokens_per_s": round(m.num_tokens / ms * 1e3, 1),
-                      "roofline_ms": round(roof_ms, 3), "frac_of_roofline": round(roof_ms / ms, 4),
-                      "decode_bytes": dbytes, "store_bytes": sbytes, "prefill_flops": flops,
-                      "slots_per_layer": d0.num_slots, "decode_context_tokens": int(d0.seq_lens.sum())}),
-          flush=True)
-    return 0
+    rec = {"mixed_step": "qwen3-8b 36 layers: 192 decode + 2x2048 prefill on 8192 prefix",
+           "ms_per_step": round(ms, 3), "steps": iters, "tokens_per_step": m.num_tokens,
+           "tokens_per_s": round(m.num_tokens / ms * 1e3, 1),
+           "roofline_ms": round(roof_ms, 3), "frac_of_roofline": round(roof_ms / ms, 4),
+           "decode_bytes": dbytes, "store_bytes": sbytes, "prefill_flops": flops,
+           "slots_per_layer": d0.num_slots, "decode_context_tokens": int(d0.seq_lens.sum())}
+    del views, d0, p0, od, op, ws, m
+    torch.cuda.empty_cache()
+    return rec
 
 
 def prefill_profile(iters: int, zero_new: bool = False) -> int:
@@ -744,6 +754,7 @@ def main() -> int:
     ap.add_argument("--chunk", type=int, default=0, help="decode split size (0 = library default)")
     ap.add_argument("--kernel-iters", type=int, default=KERNEL_ITERS, help="eager decode launches timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed 36-layer step (config 5)")
     ap.add_argument("--cpu-sample-reqs", type=int, default=256,
                     help="decode requests the CPU oracle is timed on (first N of the batch)")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
@@ -996,6 +1007,15 @@ def main() -> int:
     pflush["TFLOPs"] = round(prefill_flops(w3) / (pflush["median_ms"] * 1e-3) / 1e12, 1)
     pflush["frac_bf16_peak"] = round(pflush["TFLOPs"] / BF16_DENSE_PEAK_TFLOPS, 4)
 
+    # config 5: the mixed 36-layer step (its own 172 GB pool), unless --no-mixed
+    mixed_rec = None
+    if not args.no_mixed:
+        try:
+            mixed_rec = mixed_leg(5, stream)
+        except torch.cuda.OutOfMemoryError as e:  # the pool does not fit beside the other legs' buffers
+            torch.cuda.empty_cache()
+            mixed_rec = {"skipped": f"out of device memory: {str(e)[:120]}"}
+
     dbytes = decode_bytes(w4)
     sbytes = store_bytes(w4)
     flops3 = prefill_flops(w3)
@@ -1090,6 +1110,7 @@ def main() -> int:
         "rope_store_kv": rope,
         "vocab_embed": vocab,
         "shared_prefix_decode": cascade,
+        "mixed_step": mixed_rec,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode attention (split + merge), eager, bs 256",
