@@ -12,9 +12,12 @@
 //      fill the GPU; each range leaves a normalised float32 partial output and
 //      its lse;
 //   2. suffix pass: each request against its own keys P .. seq_len-1, on the
-//      split-K decode kernels (a per-request key start), float32 output + lse;
-//   3. merge: out = sum_i w_i o_i / sum_i w_i with w_i = exp(lse_i - max lse),
-//      lse = max + log(sum_i w_i), rounded once to bf16.
+//      split-K decode kernel (a per-request key start): float32 output + lse
+//      where one block covers the request's own keys, else the pieces'
+//      unnormalised states, left for step 3 (no decode merge runs);
+//   3. merge: out = sum_i w_i o_i / sum_i w_i with w_i = exp(lse_i - max lse)
+//      over the prefix splits and the suffix (or its pieces), lse = max +
+//      log(sum_i w_i), rounded once to bf16.
 // The result is the ordinary decode attention; only the number of times the
 // prefix's K/V rows are read changes (once per group instead of once per
 // request).
