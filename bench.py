@@ -680,7 +680,8 @@ def read_ceilings(iters: int, stream) -> None:
     loads over 4 GiB, and a 4 GiB pool of 2 KB rows (8 kv heads x 128 bf16)
     read as 256-byte per-head slices of rows in random order (page size 1) and
     of random 16-row pages (page size 16).  Each is the best over a few grid
-    sizes; one JSON line each."""
+    sizes (and, for the gathers, 4 or 8 loads in flight per lane); one JSON line
+    each."""
     import ctypes
 
     import torch
@@ -690,7 +691,7 @@ def read_ceilings(iters: int, stream) -> None:
     lib = ctypes.CDLL(_build.PROBES_PATH)
     P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.msglp_stream_read.argtypes = [P, I64, P, I, P]
-    lib.msglp_gather_heads.argtypes = [P, P, I, I, I, P, I, P]
+    lib.msglp_gather_heads.argtypes = [P, P, I, I, I, P, I, I, P]
     dev = stream.device
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     nbytes = 4 << 30
@@ -716,16 +717,21 @@ def read_ceilings(iters: int, stream) -> None:
             ("sequential read, 16-byte nontemporal loads, 4 GiB",
              lambda g: lib.msglp_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), g, s), (cus, 2 * cus, 4 * cus)),
             ("random 2 KB rows read as 256-byte head slices (page size 1), 4 GiB pool",
-             lambda g: lib.msglp_gather_heads(buf.data_ptr(), row_ids.data_ptr(), rows, heads, 0, sink.data_ptr(), g, s),
-             (cus // 4, cus // 2, cus, 2 * cus)),
+             lambda g: lib.msglp_gather_heads(buf.data_ptr(), row_ids.data_ptr(), rows, heads, 0, sink.data_ptr(),
+                                              g[0], g[1], s),
+             [(b, f) for f in (4, 8) for b in (cus // 4, cus // 2, cus, 2 * cus)]),
             ("random 16-row pages read as 256-byte head slices (page size 16), 4 GiB pool",
              lambda g: lib.msglp_gather_heads(buf.data_ptr(), page_ids.data_ptr(), rows // 16, heads, 1,
-                                              sink.data_ptr(), g, s),
-             (cus // 4, cus // 2, cus, 2 * cus))):
+                                              sink.data_ptr(), g[0], g[1], s),
+             [(b, f) for f in (4, 8) for b in (cus // 4, cus // 2, cus, 2 * cus)])):
         ms, g = best(call, grids)
         gbs = nbytes / (ms * 1e-3) / 1e9
-        print(json.dumps({"ceiling": name, "ms": round(ms, 4), "GBs": round(gbs, 1),
-                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "blocks": g}), flush=True)
+        rec = {"ceiling": name, "ms": round(ms, 4), "GBs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        if isinstance(g, tuple):
+            rec.update(blocks=g[0], loads_in_flight_per_lane=g[1])
+        else:
+            rec["blocks"] = g
+        print(json.dumps(rec), flush=True)
 
 
 def main() -> int:

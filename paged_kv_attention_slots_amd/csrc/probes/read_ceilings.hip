@@ -34,27 +34,29 @@ __global__ __launch_bounds__(256) void stream_read(const u32x4 *__restrict__ p, 
 
 // Rows of `row_vec` 16-byte vectors (kv heads x 256 bytes); head h = blockIdx.y.
 // Each group of 16 lanes reads one row's 256-byte slice of head h; a wave holds
-// 4 rows per load and 4 loads in flight.  PAGE: ids name pages of 16
-// consecutive rows, and a wave reads the 16 rows of one page (the page-size-16
-// pattern); otherwise each row id is a random row (page size 1).
-template <bool PAGE>
+// 4 rows per load and NF loads in flight.  PAGE: ids name pages of 16
+// consecutive rows, and a wave reads the 16 rows of NF / 4 pages per round (the
+// page-size-16 pattern); otherwise each row id is a random row (page size 1).
+template <bool PAGE, int NF>
 __global__ __launch_bounds__(256) void gather_heads(const u32x4 *__restrict__ pool, const int *__restrict__ ids,
                                                     int n_ids, int row_vec, unsigned *sink, int keep) {
+    static_assert(NF % 4 == 0, "whole pages per round");
     const int lane = threadIdx.x & 63, grp = lane >> 4, l = lane & 15;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * 4;
     const int h = blockIdx.y;
     unsigned acc = 0;
-    const int per_wave = PAGE ? 1 : 16;  // ids a wave consumes per round
+    const int per_wave = PAGE ? NF / 4 : 4 * NF;  // ids a wave consumes per round
     for (int r0 = wave * per_wave; r0 < n_ids; r0 += nwaves * per_wave) {
-        u32x4 v[4];
+        u32x4 v[NF];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < NF; ++k) {
             int64_t row;
             bool ok;
             if (PAGE) {
-                row = (int64_t)ids[r0] * 16 + 4 * k + grp;
-                ok = true;
+                const int r = r0 + k / 4;
+                ok = r < n_ids;
+                row = ok ? (int64_t)ids[r] * 16 + 4 * (k % 4) + grp : 0;
             } else {
                 const int r = r0 + 4 * k + grp;
                 ok = r < n_ids;
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) void gather_heads(const u32x4 *__restrict__ po
             v[k] = ok ? __builtin_nontemporal_load(pool + row * row_vec + h * 16 + l) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc ^= v[k].x ^ v[k].w;
+        for (int k = 0; k < NF; ++k) acc ^= v[k].x ^ v[k].w;
     }
     if (keep) sink[blockIdx.x & 3] = acc;
 }
@@ -80,16 +82,18 @@ extern "C" int msglp_stream_read(const void *buf, int64_t bytes, unsigned *sink,
 
 // pool: rows of heads x 256 bytes.  page == 0: ids are n_ids row ids in [0, rows);
 // page == 1: ids are n_ids page ids in [0, rows / 16).  Reads every head's slice of
-// every named row: n_ids x heads x 256 bytes (x 16 for pages).
+// every named row: n_ids x heads x 256 bytes (x 16 for pages).  inflight: 4 or 8
+// loads per lane in flight.
 extern "C" int msglp_gather_heads(const void *pool, const int *ids, int n_ids, int heads, int page, unsigned *sink,
-                                  int blocks, void *stream) {
-    if (heads < 1 || heads > 64 || n_ids < 0 || blocks < 1) return (int)hipErrorInvalidValue;
+                                  int blocks, int inflight, void *stream) {
+    if (heads < 1 || heads > 64 || n_ids < 0 || blocks < 1 || (inflight != 4 && inflight != 8))
+        return (int)hipErrorInvalidValue;
     const dim3 grid(blocks, heads);
-    if (page)
-        hipLaunchKernelGGL(gather_heads<true>, grid, dim3(256), 0, (hipStream_t)stream, (const u32x4 *)pool, ids,
-                           n_ids, heads * 16, sink, 0);
-    else
-        hipLaunchKernelGGL(gather_heads<false>, grid, dim3(256), 0, (hipStream_t)stream, (const u32x4 *)pool, ids,
-                           n_ids, heads * 16, sink, 0);
+    const hipStream_t st = (hipStream_t)stream;
+    const u32x4 *p = (const u32x4 *)pool;
+    if (page && inflight == 4) hipLaunchKernelGGL((gather_heads<true, 4>), grid, dim3(256), 0, st, p, ids, n_ids, heads * 16, sink, 0);
+    if (page && inflight == 8) hipLaunchKernelGGL((gather_heads<true, 8>), grid, dim3(256), 0, st, p, ids, n_ids, heads * 16, sink, 0);
+    if (!page && inflight == 4) hipLaunchKernelGGL((gather_heads<false, 4>), grid, dim3(256), 0, st, p, ids, n_ids, heads * 16, sink, 0);
+    if (!page && inflight == 8) hipLaunchKernelGGL((gather_heads<false, 8>), grid, dim3(256), 0, st, p, ids, n_ids, heads * 16, sink, 0);
     return (int)hipGetLastError();
 }
