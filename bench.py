@@ -404,6 +404,57 @@ def prefill_cpu_baseline(oracle, w, threads: int) -> dict:
                            "sample": f"every 32nd query row ({n_one}), {s_one:.2f} s per pass on 1 thread"}}
 
 
+def oracle_pass_time(oracle, w, n_threads: int, min_seconds: float, max_seconds: float) -> tuple:
+    """Seconds per pass of the oracle's attention over workload ``w`` (host
+    copies, store_kv applied first, outside the clock), repeated until
+    ``min_seconds`` (or before passing ``max_seconds``); and the pass count."""
+    kp, vp = oracle.store_kv(w.k_pool.cpu(), w.v_pool.cpu(), w.k_new.cpu(), w.v_new.cpu(), w.out_loc.cpu())
+    args_h = (w.q.cpu(), kp, vp, w.page_table.cpu(), w.table_idx.cpu(), w.seq_lens.cpu(), w.cu_q.cpu())
+    return oracle_pass_time_h(oracle, args_h, n_threads, min_seconds, max_seconds)
+
+
+def oracle_pass_time_h(oracle, args_h, n_threads: int, min_seconds: float, max_seconds: float) -> tuple:
+    """The same on host arguments already prepared (q, pools, page table, table_idx, seq_lens, cu_q)."""
+    prev = oracle.num_threads()
+    oracle.set_threads(n_threads)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention(*args_h)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el * (reps + 1) / reps > max_seconds:
+            break
+    oracle.set_threads(prev)
+    return el / reps, reps
+
+
+def small_config_cpu_baselines(oracle, w2, threads: int) -> dict:
+    """The oracle on the small configurations, whole: Qwen3-0.6B decode at
+    bs 64 on all threads and on one, and the tiny fp32 decode and prefill on one
+    thread (GB/s of algorithmic bytes for decode, TFLOP/s for prefill)."""
+    from paged_kv_attention_slots_amd import workloads as wl
+
+    out = {}
+    sb = decode_bytes(w2)
+    for tag, n in (("all_threads", threads), ("one_thread", 1)):
+        s, reps = oracle_pass_time(oracle, w2, n, 2.0, 6.0)
+        out[f"qwen3_06b_decode_bs64_{tag}"] = {
+            "value": round(sb / s / 1e9, 4), "unit": "GB/s", "threads": n,
+            "sample": f"the whole batch ({int(w2.seq_lens.sum())} context tokens), {reps} passes, {s:.3f} s each"}
+    t1d = wl.tiny("decode")
+    s, reps = oracle_pass_time(oracle, t1d, 1, 0.5, 2.0)
+    out["tiny_fp32_decode_one_thread"] = {"value": round(decode_bytes(t1d) / s / 1e9, 4), "unit": "GB/s",
+                                          "threads": 1, "sample": f"both requests, {reps} passes, {s * 1e6:.1f} us each"}
+    t1p = wl.tiny("prefill")
+    ext = (t1p.seq_lens - t1p.cached_lens).double()
+    fl = 4.0 * t1p.head_dim * t1p.q_heads * float((ext * t1p.cached_lens.double() + ext * (ext + 1) / 2).sum())
+    s, reps = oracle_pass_time(oracle, t1p, 1, 0.5, 2.0)
+    out["tiny_fp32_prefill_one_thread"] = {"value": round(fl / s / 1e12, 8), "unit": "TFLOP/s", "threads": 1,
+                                           "sample": f"both requests ({t1p.num_tokens} query rows), {reps} passes, "
+                                                     f"{s * 1e6:.1f} us each"}
+    return out
+
+
 def flushed_timing(fn, stream, iters: int, flush_bytes: int = 1 << 30, warm: int = 3) -> dict:
     """Per-launch times of ``fn`` with a write of ``flush_bytes`` to a scratch
     buffer before each launch (outside the events), so the last-level cache
@@ -1069,8 +1120,18 @@ def main() -> int:
                          f"in this process's affinity set)",
                "seconds_per_pass": round(cpu_s, 3)}
         log(f"  oracle {cpu_s:.2f}s with {threads} threads")
+        # the first 8 of the same requests on one thread (the pools as stored above)
+        n1 = min(8, n)
+        w1t = wl.subset_decode(ws, n1)
+        s1, r1 = oracle_pass_time_h(oracle, (q_h[:n1], kp_h, vp_h, args_h[0], args_h[1][:n1], args_h[2][:n1],
+                                             args_h[3][:n1 + 1]), 1, 2.0, 8.0)
+        cpu["one_thread"] = {"value": round(decode_bytes(w1t) / s1 / 1e9, 4), "unit": "GB/s",
+                             "sample": f"the first {n1} requests ({int(w1t.seq_lens.sum())} context tokens), "
+                                       f"{r1} passes, {s1:.2f} s each on 1 thread"}
         cpu_prefill = prefill_cpu_baseline(oracle, w3, threads)
         cpu["prefill"] = cpu_prefill
+        log("CPU oracle on the small configurations")
+        cpu["small_configs"] = small_config_cpu_baselines(oracle, w2, threads)
 
     rec = {
         "metric": "paged decode-attn achieved HBM GB/s + req-tokens/s; prefill attn TFLOP/s",
