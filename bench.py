@@ -455,7 +455,7 @@ def small_config_cpu_baselines(oracle, w2, threads: int) -> dict:
     return out
 
 
-def flushed_timing(fn, stream, iters: int, flush_bytes: int = 1 << 30, warm: int = 3) -> dict:
+def flushed_timing(fn, stream, iters: int, flush_bytes: int = 1 << 30, warm: int = 10) -> dict:
     """Per-launch times of ``fn`` with a write of ``flush_bytes`` to a scratch
     buffer before each launch (outside the events), so the last-level cache
     holds none of the kernel's inputs: median, p10 and p90 in ms."""
@@ -1050,12 +1050,12 @@ def main() -> int:
     # both attention kernels again, one launch at a time after a 1 GiB cache flush
     log("timing flushed launches (1 GiB written between launches)")
     dflush = flushed_timing(lambda: runner.decode_attn(w4, k_pool4, v_pool4, out=out4, lse=lse4, workspace=ws4,
-                                                       chunk=args.chunk, stream=stream), stream, 30)
+                                                       chunk=args.chunk, stream=stream), stream, 50)
     dflush["GBs"] = round(decode_bytes(w4) / (dflush["median_ms"] * 1e-3) / 1e9, 1)
     # the captured steps at both page sizes, replayed one at a time after the flush
     gflush = {}
     for tag, w, g in ((f"ps{w4.page_size}", w4, graph), (f"ps{w4o.page_size}", w4o, g_o)):
-        f = flushed_timing(lambda g=g: g.launch(stream), stream, 30)
+        f = flushed_timing(lambda g=g: g.launch(stream), stream, 50)
         gbs = (decode_bytes(w) + store_bytes(w)) / (f["median_ms"] * 1e-3) / 1e9
         f["GBs"] = round(gbs, 1)
         f["frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
