@@ -455,30 +455,49 @@ def small_config_cpu_baselines(oracle, w2, threads: int) -> dict:
     return out
 
 
-def flushed_timing(fn, stream, iters: int, flush_bytes: int = 1 << 30, warm: int = 10) -> dict:
-    """Per-launch times of ``fn`` with a write of ``flush_bytes`` to a scratch
-    buffer before each launch (outside the events), so the last-level cache
-    holds none of the kernel's inputs: median, p10 and p90 in ms."""
+def flushed_timing(fn, stream, iters: int, flush_bytes: int = 1 << 30, warm: int = 10,
+                   read_bytes: int = 1 << 29) -> dict:
+    """Per-launch times of ``fn``, each after a cache flush outside the events:
+    a write of ``flush_bytes`` to a scratch buffer, then a read of
+    ``read_bytes`` from another, so that the last-level cache (256 MB) holds
+    none of the kernel's inputs and no dirty lines.  A flush by writes alone
+    leaves up to a cache's worth of dirty lines, whose write-back then lands
+    inside the timed launch; that variant is timed too and reported under
+    ``write_only``.  Median, p10 and p90 in ms."""
     import torch
 
     scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device=stream.device)
+    clean = torch.ones(read_bytes // 4, dtype=torch.float32, device=stream.device)
+    sink = torch.empty((), dtype=torch.float32, device=stream.device)
+    torch.cuda.synchronize()
     for _ in range(warm):
         fn()
-    times = []
-    for _ in range(iters):
-        with torch.cuda.stream(stream):
-            scratch.fill_(1.0)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        fn()
-        b.record(stream)
-        b.synchronize()
-        times.append(a.elapsed_time(b))
-    del scratch
-    times.sort()
-    q = lambda f: times[min(len(times) - 1, int(f * (len(times) - 1) + 0.5))]
-    return {"median_ms": round(q(0.5), 4), "p10_ms": round(q(0.1), 4), "p90_ms": round(q(0.9), 4),
-            "iters": iters, "flush_bytes": flush_bytes}
+
+    def run(read_after: bool) -> list:
+        times = []
+        for _ in range(iters):
+            with torch.cuda.stream(stream):
+                scratch.fill_(1.0)
+                if read_after:
+                    torch.sum(clean, dim=0, out=sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        times.sort()
+        return times
+
+    times = run(True)
+    times_w = run(False)
+    del scratch, clean, sink
+    q = lambda t, f: t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))]
+    return {"median_ms": round(q(times, 0.5), 4), "p10_ms": round(q(times, 0.1), 4), "p90_ms": round(q(times, 0.9), 4),
+            "iters": iters, "flush_bytes": flush_bytes,
+            "flush": f"write {flush_bytes >> 20} MiB, then read {read_bytes >> 20} MiB of another buffer",
+            "write_only": {"median_ms": round(q(times_w, 0.5), 4), "p10_ms": round(q(times_w, 0.1), 4),
+                           "p90_ms": round(q(times_w, 0.9), 4)}}
 
 
 def sweep(iters: int) -> int:
@@ -1047,8 +1066,9 @@ def main() -> int:
     log("building the shared-prefix decode batch and timing it")
     cascade = shared_prefix_leg(args.kernel_iters, stream)
 
-    # both attention kernels again, one launch at a time after a 1 GiB cache flush
-    log("timing flushed launches (1 GiB written between launches)")
+    # both attention kernels again, one launch at a time after a cache flush (1 GiB written,
+    # then 512 MiB read: no input and no dirty line left in the last-level cache)
+    log("timing flushed launches (1 GiB written and 512 MiB read between launches)")
     dflush = flushed_timing(lambda: runner.decode_attn(w4, k_pool4, v_pool4, out=out4, lse=lse4, workspace=ws4,
                                                        chunk=args.chunk, stream=stream), stream, 50)
     dflush["GBs"] = round(decode_bytes(w4) / (dflush["median_ms"] * 1e-3) / 1e9, 1)
@@ -1059,6 +1079,8 @@ def main() -> int:
         gbs = (decode_bytes(w) + store_bytes(w)) / (f["median_ms"] * 1e-3) / 1e9
         f["GBs"] = round(gbs, 1)
         f["frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+        f["write_only"]["frac_hbm"] = round((decode_bytes(w) + store_bytes(w)) / (f["write_only"]["median_ms"] * 1e-3)
+                                            / 1e9 / HBM_PEAK_GBS, 4)
         gflush[tag] = f
     pflush = flushed_timing(prefill_attn_only, stream, 50)
     pflush["TFLOPs"] = round(prefill_flops(w3) / (pflush["median_ms"] * 1e-3) / 1e12, 1)
